@@ -1,0 +1,8 @@
+"""Seeded synthetic workloads shared by the tests, the smoke check and the benchmark.
+
+Holds shapes, seeds and random draws only; no part of the method is computed here.
+"""
+from .configs import (ALL, BY_NAME, CHUNKED_128K, DECODE_128K, PAGED_DECODE_MIXED,  # noqa: F401
+                      PREFILL_32K, SMALL_CHUNKED, SMALL_DECODE, SMALL_PAGED, SMALL_PREFILL,
+                      TINY_PREFILL, Workload)
+from .gen import Inputs, cache_of, generate, quantize_e4m3fn, sample_rows  # noqa: F401
