@@ -1,0 +1,229 @@
+#!/usr/bin/env python3
+"""Benchmark of the DSA hot path on one MI355X: batched decode at 128K context.
+
+One step = one fused dsa_decode call over the whole batch: lightning indexer
+over every cached token of every sequence, top-k (k = 2048), sparse MQA
+attention over the selected rows, with inputs already resident in HBM.
+
+Prints ONE JSON line (rank 0) with the throughput (queries/s), the roofline
+of the dominant kernel (the indexer, HBM-bound) measured with HIP events
+inside the timed region, per-stage times, and the CPU oracle timed on a
+bounded sample of the same workload.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload decode_b32_ctx128k]
+                    [--no-cpu-baseline] [--copy-calibration BYTES]
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, vendor figure
+
+
+def _hip():
+    lib = ctypes.CDLL("libamdhip64.so")
+    lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+    lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+    lib.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+    lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+    return lib
+
+
+def decode_bytes_per_query(wl, ctx):
+    """Algorithmic HBM bytes of one decode query over `ctx` cached tokens.
+
+    index keys + key scales (every token once), the k gathered latent KV rows,
+    q, out, and the indexer query (q8, w, q_scale).  Scores and indices are
+    intermediate and not counted.
+    """
+    idx_keys = ctx * (wl.d_I + 4)
+    kv = min(wl.k, ctx) * wl.D * 2
+    q = wl.H * wl.D * 2
+    out = wl.H * wl.D_v * 2
+    iq = wl.H_I * wl.d_I + wl.H_I * 4 + 4
+    return idx_keys, kv + q + out + iq
+
+
+def run_bench(args):
+    import torch
+
+    import workloads as W
+    import sparse_attention_long_06_amd as dsa
+    from sparse_attention_long_06_amd import _lib
+
+    wl = W.BY_NAME[args.workload]
+    if wl.kind != "decode":
+        raise SystemExit(f"bench.py times the decode path; {wl.name} is a {wl.kind} workload")
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    print(f"[bench] generating {wl.name} on {dev}", file=sys.stderr, flush=True)
+    inp = W.generate(wl, dev)
+    batch = dsa.Batch.from_inputs(inp)
+    B = inp.num_rows
+    out = torch.empty((B, wl.H, wl.D_v), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((B, wl.H), dtype=torch.float32, device=dev)
+    idx = torch.empty((B, wl.k), dtype=torch.int32, device=dev)
+    ws_n = dsa.workspace_size(dsa.DSA_WS_DECODE, batch, wl.k, wl.H, wl.D_v)
+    ws = torch.empty(ws_n, dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+
+    def step():
+        dsa.decode(batch, inp.q8, inp.q_scale, inp.w, inp.k8, inp.k_scale, wl.k, inp.q, inp.kv, inp.v,
+                   wl.scale, out=out, lse=lse, idx_out=idx, workspace=ws, D_v=wl.D_v)
+
+    print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # stage events for every timed step (recorded by the library on its stream)
+    hip = _hip()
+    lib = _lib.load()
+    events = []
+    for _ in range(4 * args.steps):
+        ev = ctypes.c_void_p()
+        assert hip.hipEventCreate(ctypes.byref(ev)) == 0
+        events.append(ev.value)
+    step_events = [(ctypes.c_void_p * 4)(*events[4 * i: 4 * i + 4]) for i in range(args.steps)]
+
+    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        assert lib.dsa_set_stage_events(step_events[i], 4) == 0
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    elapsed = t1 - t0
+
+    stage_ms = {"indexer": 0.0, "topk": 0.0, "attention": 0.0}
+    f = ctypes.c_float()
+    for i in range(args.steps):
+        e = events[4 * i: 4 * i + 4]
+        for name, (a, b) in zip(stage_ms, [(0, 1), (1, 2), (2, 3)]):
+            assert hip.hipEventElapsedTime(ctypes.byref(f), ctypes.c_void_p(e[a]), ctypes.c_void_p(e[b])) == 0
+            stage_ms[name] += f.value / args.steps
+    for ev in events:
+        hip.hipEventDestroy(ctypes.c_void_p(ev))
+
+    ms = elapsed * 1e3 / args.steps
+    qps = B / (elapsed / args.steps)
+    ctx_total = sum(inp.seq_lens_host)
+    idx_bytes = sum(decode_bytes_per_query(wl, L)[0] for L in inp.seq_lens_host)
+    other_bytes = sum(decode_bytes_per_query(wl, L)[1] for L in inp.seq_lens_host)
+    idx_gbs = idx_bytes / (stage_ms["indexer"] * 1e-3) / 1e9
+    step_gbs = (idx_bytes + other_bytes) / (ms * 1e-3) / 1e9
+    att_bytes = other_bytes - B * (wl.H_I * wl.d_I + wl.H_I * 4 + 4)
+    att_gbs = att_bytes / (stage_ms["attention"] * 1e-3) / 1e9
+    att_flops = sum(2 * wl.H * min(wl.k, L) * (wl.D + wl.D_v) for L in inp.seq_lens_host)
+    idx_flops = sum(2 * wl.H_I * wl.d_I * L for L in inp.seq_lens_host)
+
+    res = {
+        "metric": "DSA decode queries/s @128K ctx, k=2048; indexer TFLOPS + attn HBM GB/s",
+        "value": round(qps, 1),
+        "unit": "queries/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8-storage/bf16-mfma",
+        "data": "synthetic (seeded N(0,1) draws, per-token e4m3fn quantised indexer q/k; bf16 latent KV)",
+        "config": {"workload": wl.name, "queries": B, "context": wl.seq_len, "k": wl.k, "H_I": wl.H_I,
+                   "d_I": wl.d_I, "H": wl.H, "D": wl.D, "D_v": wl.D_v, "paged": wl.paged,
+                   "parallelism": "single GPU"},
+        "tokens_per_s": round(qps, 1),
+        "context_tokens_scanned_per_s": round(ctx_total / (elapsed / args.steps), 1),
+        "roofline": {"bound": "hbm", "kernel": "indexer_kernel (decode layout, fused top-k histogram)",
+                     "achieved": round(idx_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(idx_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "bytes_per_launch": idx_bytes, "launch_ms": round(stage_ms["indexer"], 4)},
+        "stages_ms": {k: round(v, 4) for k, v in stage_ms.items()},
+        "step_hbm": {"bytes": idx_bytes + other_bytes, "GB/s": round(step_gbs, 1),
+                     "frac": round(step_gbs / HBM_PEAK_GBS, 4)},
+        "indexer_tflops": round(idx_flops / (stage_ms["indexer"] * 1e-3) / 1e12, 2),
+        "attention": {"GB/s": round(att_gbs, 1), "hbm_frac": round(att_gbs / HBM_PEAK_GBS, 4),
+                      "TFLOP/s": round(att_flops / (stage_ms["attention"] * 1e-3) / 1e12, 2)},
+    }
+    del ws, out, lse
+    return res, inp
+
+
+def cpu_baseline(inp, budget_s: float):
+    """Time the CPU oracle on whole decode queries until ~budget_s of work is done."""
+    import oracle
+    from tests.oracle_io import arrays_of
+
+    wl = inp.wl
+    B = inp.num_rows
+    a = arrays_of(inp.to("cpu"))      # host copies: input preparation, not timed
+    try:
+        import threadpoolctl
+        threads = max(i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()) or os.cpu_count()
+    except Exception:  # noqa: BLE001
+        threads = os.cpu_count()
+    done = 0
+    t0 = time.perf_counter()
+    for r in range(B):
+        oracle.run_rows(a, [r])
+        done += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    el = time.perf_counter() - t0
+    return {"value": round(done / el, 4), "unit": "queries/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{done} of {B} decode queries of {wl.name} (each: indexer over {wl.seq_len} tokens, "
+                      f"top-{wl.k}, attention), fp64 NumPy, {el:.1f} s"}
+
+
+def copy_calibration(nbytes: int):
+    """A plain device copy of known size, for scaling FETCH_SIZE / WRITE_SIZE counters."""
+    import torch
+    src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda:0").fill_(1.0)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": nbytes, "launches": 3}))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="decode_b32_ctx128k")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--copy-calibration", type=int, default=0)
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this build measures one GPU only: the DSA path here has no multi-GPU "
+                                   "mode (see DESIGN.md for how it would shard); run with --gpus 1"}))
+        raise SystemExit(2)
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
+    res, inp = run_bench(args)
+    if not args.no_cpu_baseline:
+        print("[bench] cpu oracle baseline", file=sys.stderr, flush=True)
+        res["cpu_baseline"] = cpu_baseline(inp, args.cpu_budget)
+    else:
+        res["cpu_baseline"] = None
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

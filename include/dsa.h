@@ -1,0 +1,188 @@
+/*
+ * dsa.h — C ABI of the DeepSeek Sparse Attention (DSA) hot path for AMD
+ * Instinct MI355X (gfx950).
+ *
+ * The path has three stages (ouchyi.pink post on DSA, the DSA paragraph;
+ * tenelement.pl article "DeepSeek V3.2-Exp Cuts Long-Context Costs with
+ * DeepSeek Sparse Attention (DSA) While Maintaining Benchmark Parity",
+ * section "Architektura DeepSeek V3.2-Exp: Od MoE do DSA"):
+ *
+ *   1. dsa_indexer     — the lightning indexer: a few FP8 heads score every
+ *                        cached token for each query row,
+ *                          I[t,s] = k_scale[s] * sum_j (w[t,j]*q_scale[t]) * ReLU(q8[t,j] . k8[s])
+ *   2. dsa_topk        — keep k tokens per query row (k = 2048 on the pages,
+ *                        whatever the context length),
+ *   3. dsa_sparse_attn — softmax attention over only the kept tokens, in MQA
+ *                        form: all query heads read one shared latent KV row
+ *                        per token (same article, same section; degnora.com
+ *                        "DeepSeekV3, Farkı Ne?", section "MLA — Multi-Latent
+ *                        Attention").
+ *   dsa_decode chains the three for one query per sequence without any host
+ *   round trip between the stages (sider.ai "Sparse attention that isn't
+ *   sparse thinking", sections "Uyarılar" and "Dağıtım Gerçekliği": selection
+ *   that bounces between CPU and GPU, or launch overhead, eats the gain).
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * - All tensor pointers are DEVICE pointers owned by the caller; the library
+ *   never allocates, frees, copies to the host or synchronises.  All work is
+ *   enqueued on `stream` (a hipStream_t; NULL = the default stream) and the
+ *   buffers must stay alive until that work has completed.
+ * - Query rows are grouped by sequence.  Sequence b has seq_lens[b] cached
+ *   tokens; its query rows are its LAST nq_b tokens, so row i of sequence b
+ *   sits at position p = seq_lens[b] - nq_b + i and sees tokens 0..p
+ *   (causal, itself included).  With q_start == NULL there is exactly one
+ *   query row per sequence (row b, position seq_lens[b]-1): decode.
+ * - Caches are contiguous per sequence or paged.  Token s of sequence b is
+ *   token row r of a cache, where r = b*seq_stride + s when block_table is
+ *   NULL, else r = block_table[b*max_blocks + s/block_size]*block_size +
+ *   s%block_size.  Its bytes start at data + r*row_stride.  One batch (and so
+ *   one block table) describes all caches of a call.
+ * - Scalars: FP8 is OCP e4m3fn bytes; bf16 is passed as its 16-bit pattern.
+ * - Errors: arguments are validated on the host before anything is enqueued;
+ *   a non-OK status leaves every output untouched and dsa_last_error()
+ *   (thread-local) describes it.  DSA_ERR_HIP reports a failed launch.
+ *   Device faults surface at the caller's next synchronisation.  Nothing is
+ *   printed, thrown or aborted across this interface.
+ * - Results are deterministic: the same inputs give bit-identical outputs.
+ */
+#ifndef DSA_H_
+#define DSA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum dsa_status {
+  DSA_OK = 0,
+  DSA_ERR_NULL = 1,        /* a required pointer is NULL */
+  DSA_ERR_SHAPE = 2,       /* inconsistent sizes, strides or bounds */
+  DSA_ERR_UNSUPPORTED = 3, /* valid, but no kernel for these sizes */
+  DSA_ERR_ALIGN = 4,       /* pointer or stride not aligned as required */
+  DSA_ERR_WORKSPACE = 5,   /* workspace missing or smaller than dsa_workspace_size() */
+  DSA_ERR_HIP = 6          /* a HIP launch failed */
+} dsa_status;
+
+/* Token rows of one cache (index keys, key scales, latent KV, separate V). */
+typedef struct dsa_cache {
+  const void* data;   /* device pointer to token row 0 */
+  int64_t row_stride; /* bytes between consecutive token rows */
+  int64_t seq_stride; /* contiguous caches: token rows between sequences (unused when paged) */
+} dsa_cache;
+
+/* Batch geometry: sequences, query rows and (optionally) the page table. */
+typedef struct dsa_batch {
+  int32_t num_seqs;           /* B >= 1 */
+  int32_t num_rows;           /* T: total query rows (== B when q_start is NULL) */
+  int32_t max_q;              /* host bound on nq_b (1 when q_start is NULL) */
+  int32_t max_len;            /* host bound on seq_lens[b]; sizes grids and checks ld */
+  const int32_t* seq_lens;    /* device [B]: 1 <= seq_lens[b] <= max_len */
+  const int32_t* q_start;     /* device [B+1] row offsets, or NULL (one row per sequence) */
+  const int32_t* block_table; /* device [B, max_blocks] physical block ids, or NULL */
+  int32_t max_blocks;         /* paged: entries per table row */
+  int32_t block_size;         /* paged: tokens per block, a power of two >= 16 */
+} dsa_batch;
+
+/*
+ * dsa_indexer — lightning-indexer scores for every query row and every token
+ * it may see (ouchyi.pink post, DSA paragraph: few heads, FP8, cheap;
+ * tenelement.pl article, section "Architektura DeepSeek V3.2-Exp: Od MoE do
+ * DSA": logits per context token with a ReLU).
+ *   q8      [T, H_I, d_I] e4m3fn, row-major
+ *   q_scale [T] fp32 per-token dequantisation scale, or NULL (= 1)
+ *   w       [T, H_I] fp32 head weights
+ *   kidx    d_I e4m3fn bytes per token; data and row_stride 16-byte aligned
+ *   kscale  one fp32 per token (row_stride >= 4), or NULL (= 1)
+ *   scores  [T, ld] fp32 out: scores[t*ld + s] for s <= p_t; entries past
+ *           p_t are unspecified.  ld >= max_len.
+ * Supported: 1 <= H_I <= 64, d_I in {32, 128}.
+ */
+dsa_status dsa_indexer(const dsa_batch* batch, const uint8_t* q8, const float* q_scale,
+                       const float* w, const dsa_cache* kidx, const dsa_cache* kscale,
+                       int H_I, int d_I, float* scores, int64_t ld, void* stream);
+
+/*
+ * dsa_topk — per query row, the first min(k, p+1) tokens in the order
+ * (score descending, token index ascending; -0.0 equals +0.0), written in
+ * ascending token order and padded with -1 (ouchyi.pink post, DSA paragraph:
+ * a fixed number of tokens per query; digitalreport.com.tr article "DeepSeek
+ * V3.2-exp: daha ucuz uzun bağlamlı AI": fine-grained token selection).
+ *   scores  [T, ld] fp32 as written by dsa_indexer (NaN not allowed)
+ *   idx     [T, k] int32 out
+ *   workspace: dsa_workspace_size(DSA_WS_TOPK, ...) bytes, 256-byte aligned
+ * Supported: 1 <= k <= 4096.
+ */
+dsa_status dsa_topk(const dsa_batch* batch, const float* scores, int64_t ld, int k,
+                    int32_t* idx, void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * dsa_sparse_attn — softmax attention of H query heads over the selected
+ * tokens only, all heads sharing one KV row per token (MQA over the latent
+ * cache; tenelement.pl article, section "Architektura DeepSeek V3.2-Exp: Od
+ * MoE do DSA"; degnora.com "DeepSeekV3, Farkı Ne?", section "MLA —
+ * Multi-Latent Attention").
+ *   q     [T, H, D] bf16
+ *   kv    D bf16 per token (K is the whole row); 16-byte aligned rows
+ *   v     D_v bf16 per token, or NULL: V is the first D_v dims of the kv row
+ *         (a separate V cache is supported for D = 64 only)
+ *   idx   [T, k] int32 token indices; -1, and any index outside [0, p_t],
+ *         marks an unused slot
+ *   out   [T, H, D_v] bf16;  lse [T, H] fp32 natural-log softmax denominator, or NULL
+ *   workspace: dsa_workspace_size(DSA_WS_ATTN, ...) bytes (0 is valid when it says 0)
+ * A row whose k slots are all -1 gets out = 0 and lse = -inf.
+ * Supported: (D, D_v) in {(64, 64), (576, 512)}, 1 <= H <= 128, 1 <= k <= 4096.
+ */
+dsa_status dsa_sparse_attn(const dsa_batch* batch, const uint16_t* q, const dsa_cache* kv,
+                           const dsa_cache* v, int H, int D, int D_v, float scale,
+                           const int32_t* idx, int k, uint16_t* out, float* lse,
+                           void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * dsa_decode — the whole path for one query per sequence (q_start must be
+ * NULL), enqueued back to back with no host synchronisation: indexer scores
+ * (kept in the workspace), top-k, sparse attention.
+ * Arguments as in the three calls above; idx_out [B, k] receives the
+ * selected indices when not NULL.
+ */
+dsa_status dsa_decode(const dsa_batch* batch, const uint8_t* q8, const float* q_scale,
+                      const float* w, const dsa_cache* kidx, const dsa_cache* kscale,
+                      int H_I, int d_I, int k, const uint16_t* q, const dsa_cache* kv,
+                      const dsa_cache* v, int H, int D, int D_v, float scale,
+                      uint16_t* out, float* lse, int32_t* idx_out,
+                      void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * dsa_set_stage_events — opt-in stage timing for the NEXT dsa_decode call on
+ * this thread (for profiling tools; the stages are the ones the pages name:
+ * indexer, selection, core attention).  `events` holds `count` >= 4 hipEvent_t
+ * handles created by the caller; dsa_decode records them on its stream:
+ *   events[0] before the indexer (after the workspace clear),
+ *   events[1] after the indexer, events[2] after the top-k,
+ *   events[3] after the attention (and its split combine).
+ * The registration is consumed by that one call.  NULL clears it.
+ * Errors: DSA_ERR_SHAPE if count < 4.  A failed record returns DSA_ERR_HIP
+ * from dsa_decode.
+ */
+dsa_status dsa_set_stage_events(void* const* events, int count);
+
+/* Which call dsa_workspace_size() sizes. */
+enum { DSA_WS_TOPK = 1, DSA_WS_ATTN = 2, DSA_WS_DECODE = 3 };
+
+/*
+ * Workspace bytes `entry` needs for this batch (host-only; no device call).
+ * H and D_v matter for DSA_WS_ATTN / DSA_WS_DECODE only.  Returns 0 when the
+ * call needs none, and (size_t)-1 for invalid arguments.
+ */
+size_t dsa_workspace_size(int entry, const dsa_batch* batch, int k, int H, int D_v);
+
+/* Text for the last non-OK status returned on this thread ("" if none). */
+const char* dsa_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DSA_H_ */

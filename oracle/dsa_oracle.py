@@ -224,12 +224,13 @@ def run_rows(a: dict, rows, select_dtype=np.float32, need=("scores", "idx", "out
     k = int(a["k"])
     res = {"scores": [], "idx": [], "out": [], "lse": []}
 
-    def att_rows(name, b, n):
+    def att_rows(name, b, n, sel):
+        """Rows `sel` (logical token indices) of sequence b's cache `name`, as float64."""
         if a.get(name + "_f") is not None:
-            return token_rows(a[name + "_f"], b, n, table, bs).astype(np.float64)
+            return token_rows(a[name + "_f"], b, n, table, bs)[sel].astype(np.float64)
         if a.get(name) is None:
             return None
-        return decode_bf16(token_rows(a[name], b, n, table, bs))
+        return decode_bf16(token_rows(a[name], b, n, table, bs)[sel])
 
     for t in rows:
         b, p = geo[t]
@@ -245,9 +246,9 @@ def run_rows(a: dict, rows, select_dtype=np.float32, need=("scores", "idx", "out
         if "out" in need:
             use = idx if idx_override is None or t not in idx_override else idx_override[t]
             sel = use[use >= 0]
-            K = att_rows("kv", b, n)[sel]
-            V = att_rows("v", b, n)
-            V = K[:, : int(a["D_v"])] if V is None else V[sel]
+            K = att_rows("kv", b, n, sel)
+            V = att_rows("v", b, n, sel)
+            V = K[:, : int(a["D_v"])] if V is None else V
             if a.get("q_f") is not None:
                 qrow = a["q_f"][t].astype(np.float64)
             else:

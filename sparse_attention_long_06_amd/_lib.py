@@ -1,0 +1,63 @@
+"""ctypes view of libdsa.so and of the structs declared in include/dsa.h."""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libdsa.so")
+
+DSA_OK, DSA_ERR_NULL, DSA_ERR_SHAPE, DSA_ERR_UNSUPPORTED, DSA_ERR_ALIGN, DSA_ERR_WORKSPACE, DSA_ERR_HIP = range(7)
+STATUS_NAMES = ["DSA_OK", "DSA_ERR_NULL", "DSA_ERR_SHAPE", "DSA_ERR_UNSUPPORTED", "DSA_ERR_ALIGN",
+                "DSA_ERR_WORKSPACE", "DSA_ERR_HIP"]
+DSA_WS_TOPK, DSA_WS_ATTN, DSA_WS_DECODE = 1, 2, 3
+
+
+class DsaCache(ctypes.Structure):
+    _fields_ = [("data", ctypes.c_void_p), ("row_stride", ctypes.c_int64), ("seq_stride", ctypes.c_int64)]
+
+
+class DsaBatch(ctypes.Structure):
+    _fields_ = [("num_seqs", ctypes.c_int32), ("num_rows", ctypes.c_int32), ("max_q", ctypes.c_int32),
+                ("max_len", ctypes.c_int32), ("seq_lens", ctypes.c_void_p), ("q_start", ctypes.c_void_p),
+                ("block_table", ctypes.c_void_p), ("max_blocks", ctypes.c_int32), ("block_size", ctypes.c_int32)]
+
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+_I64 = ctypes.c_int64
+_SZ = ctypes.c_size_t
+_F = ctypes.c_float
+_BP = ctypes.POINTER(DsaBatch)
+_CP = ctypes.POINTER(DsaCache)
+
+SIGNATURES = {
+    "dsa_indexer": ([_BP, _P, _P, _P, _CP, _CP, _I, _I, _P, _I64, _P], _I),
+    "dsa_topk": ([_BP, _P, _I64, _I, _P, _P, _SZ, _P], _I),
+    "dsa_sparse_attn": ([_BP, _P, _CP, _CP, _I, _I, _I, _F, _P, _I, _P, _P, _P, _SZ, _P], _I),
+    "dsa_decode": ([_BP, _P, _P, _P, _CP, _CP, _I, _I, _I, _P, _CP, _CP, _I, _I, _I, _F, _P, _P, _P, _P, _SZ, _P],
+                   _I),
+    "dsa_workspace_size": ([_I, _BP, _I, _I, _I], _SZ),
+    "dsa_set_stage_events": ([ctypes.POINTER(ctypes.c_void_p), _I], _I),
+    "dsa_last_error": ([], ctypes.c_char_p),
+}
+
+_lib = None
+
+
+def load(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libdsa.so; raises if it has not been built.  There is no fallback path."""
+    global _lib
+    if _lib is not None and path == LIB_PATH:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with `python -m sparse_attention_long_06_amd.build` "
+                           "(the DSA path runs only in its HIP kernels)")
+    lib = ctypes.CDLL(path)
+    for name, (args, res) in SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = res
+    if path == LIB_PATH:
+        _lib = lib
+    return lib

@@ -1,0 +1,452 @@
+// C ABI of the DSA hot path: host-side validation, workspace layout and the
+// launch sequence of each entry point.  Every argument check happens before
+// the first HIP call, so an invalid call has no device side effects.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <string>
+
+#include "dsa.h"
+#include "dsa_kernels.h"
+
+using namespace dsa;
+
+namespace {
+
+thread_local std::string g_err;
+thread_local hipEvent_t g_stage_events[4] = {nullptr, nullptr, nullptr, nullptr};
+thread_local bool g_stage_armed = false;
+
+dsa_status fail(dsa_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return s;
+}
+
+dsa_status ok() {
+  g_err.clear();
+  return DSA_OK;
+}
+
+#define CHECK(cond, status, ...) \
+  do {                           \
+    if (!(cond)) return fail(status, __VA_ARGS__); \
+  } while (0)
+
+#define LAUNCH(expr, what)                                                              \
+  do {                                                                                  \
+    const hipError_t e_ = (expr);                                                       \
+    if (e_ != hipSuccess) return fail(DSA_ERR_HIP, "%s: %s", what, hipGetErrorString(e_)); \
+  } while (0)
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+bool pow2(int64_t x) { return x > 0 && (x & (x - 1)) == 0; }
+int64_t round_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
+int ilog2(int64_t x) { int r = 0; while ((int64_t(1) << r) < x) ++r; return r; }
+
+dsa_status check_batch(const dsa_batch* b) {
+  CHECK(b, DSA_ERR_NULL, "batch is NULL");
+  CHECK(b->seq_lens, DSA_ERR_NULL, "batch->seq_lens is NULL");
+  CHECK(b->num_seqs >= 1 && b->num_seqs <= 65535, DSA_ERR_SHAPE, "num_seqs %d outside [1, 65535]", b->num_seqs);
+  CHECK(b->max_len >= 1, DSA_ERR_SHAPE, "max_len %d < 1", b->max_len);
+  if (!b->q_start) {
+    CHECK(b->num_rows == b->num_seqs, DSA_ERR_SHAPE,
+          "num_rows %d != num_seqs %d with one query row per sequence", b->num_rows, b->num_seqs);
+  } else {
+    CHECK(b->num_rows >= 0, DSA_ERR_SHAPE, "num_rows %d < 0", b->num_rows);
+    CHECK(b->max_q >= 1 && b->max_q <= b->max_len, DSA_ERR_SHAPE, "max_q %d outside [1, max_len]", b->max_q);
+  }
+  if (b->block_table) {
+    CHECK(pow2(b->block_size) && b->block_size >= 16 && b->block_size <= (1 << 20), DSA_ERR_SHAPE,
+          "block_size %d is not a power of two in [16, 2^20]", b->block_size);
+    CHECK(b->max_blocks >= 1 && (int64_t)b->max_blocks * b->block_size >= b->max_len, DSA_ERR_SHAPE,
+          "max_blocks %d * block_size %d < max_len %d", b->max_blocks, b->block_size, b->max_len);
+  }
+  return DSA_OK;
+}
+
+dsa_status check_cache(const dsa_batch* b, const dsa_cache* c, const char* name, int64_t row_bytes, size_t align) {
+  CHECK(c && c->data, DSA_ERR_NULL, "%s cache is NULL", name);
+  CHECK(c->row_stride >= row_bytes, DSA_ERR_SHAPE, "%s row_stride %lld < %lld bytes", name,
+        (long long)c->row_stride, (long long)row_bytes);
+  CHECK(aligned(c->data, align) && c->row_stride % (int64_t)align == 0, DSA_ERR_ALIGN,
+        "%s data/row_stride not %zu-byte aligned", name, align);
+  if (!b->block_table)
+    CHECK(c->seq_stride >= b->max_len, DSA_ERR_SHAPE, "%s seq_stride %lld < max_len %d", name,
+          (long long)c->seq_stride, b->max_len);
+  return DSA_OK;
+}
+
+Geo make_geo(const dsa_batch* b) {
+  Geo g;
+  g.seq_lens = b->seq_lens;
+  g.q_start = b->q_start;
+  g.block_table = b->block_table;
+  g.max_blocks = b->max_blocks;
+  g.block_shift = b->block_table ? ilog2(b->block_size) : 0;
+  g.num_seqs = b->num_seqs;
+  g.num_rows = b->num_rows;
+  return g;
+}
+
+Cache make_cache(const dsa_cache* c) {
+  Cache r;
+  r.data = c ? static_cast<const char*>(c->data) : nullptr;
+  r.row_stride = c ? c->row_stride : 0;
+  r.seq_stride = c ? c->seq_stride : 0;
+  return r;
+}
+
+// ---------------------------------------------------------------- workspace plans
+
+struct TopkPlan {
+  bool split = false;
+  int nslices = 0, slice = 0;
+  size_t off_hist = 0, off_cnt = 0, off_slice = 0, off_lists = 0, bytes = 0;
+  size_t zero_words = 0;  // hist + counters + slice counts, contiguous from off_hist
+};
+
+TopkPlan plan_topk(int T, int max_len, int k) {
+  TopkPlan p;
+  if (T > kTopkSplitMaxRows || max_len <= k || T == 0) return p;
+  p.split = true;
+  const int target = (kTopkSplitMaxRows + T - 1) / T;           // slices per row for ~512 workgroups
+  int slice = (int)round_up((max_len + target - 1) / target, 1024);
+  if (slice < 1024) slice = 1024;
+  int ns = (max_len + slice - 1) / slice;
+  if (ns > kTopkMaxSlices) {
+    slice = (int)round_up((max_len + kTopkMaxSlices - 1) / kTopkMaxSlices, 1024);
+    ns = (max_len + slice - 1) / slice;
+  }
+  p.slice = slice;
+  p.nslices = ns;
+  size_t o = 0;
+  p.off_hist = o; o += (size_t)T * kBins1 * 4;
+  p.off_cnt = o; o += (size_t)T * 4;
+  p.off_slice = o; o += (size_t)T * ns * 4;
+  p.zero_words = o / 4;
+  o = (size_t)round_up((int64_t)o, 256);
+  p.off_lists = o; o += (size_t)T * ns * slice * 8;
+  p.bytes = (size_t)round_up((int64_t)o, 256);
+  return p;
+}
+
+struct AttnPlan {
+  int nsplit = 1, per_split = 0;
+  size_t off_o = 0, off_lse = 0, bytes = 0;
+};
+
+AttnPlan plan_attn(int T, int k, int H, int D_v) {
+  AttnPlan p;
+  const int blocks = (k + kAttnBlock - 1) / kAttnBlock;
+  int ns = 1;
+  if (T > 0 && T < 256) {
+    while (ns < blocks && (int64_t)T * ns < 256) ns *= 2;
+    if (ns > blocks) ns = blocks;
+  }
+  while ((k + ns - 1) / ns > kAttnMaxSplit) ++ns;
+  int per = (int)round_up((k + ns - 1) / ns, kAttnBlock);
+  ns = (k + per - 1) / per;
+  p.nsplit = ns;
+  p.per_split = per;
+  if (ns > 1) {
+    size_t o = 0;
+    p.off_o = o; o += (size_t)T * ns * H * D_v * 2;
+    o = (size_t)round_up((int64_t)o, 256);
+    p.off_lse = o; o += (size_t)T * ns * H * 4;
+    p.bytes = (size_t)round_up((int64_t)o, 256);
+  }
+  return p;
+}
+
+struct DecodePlan {
+  int64_t ld = 0;
+  TopkPlan tk;
+  AttnPlan at;
+  size_t off_scores = 0, off_topk = 0, off_idx = 0, off_attn = 0, bytes = 0;
+};
+
+DecodePlan plan_decode(int B, int max_len, int k, int H, int D_v) {
+  DecodePlan p;
+  p.ld = round_up(max_len, 4);
+  p.tk = plan_topk(B, max_len, k);
+  p.at = plan_attn(B, k, H, D_v);
+  size_t o = 0;
+  p.off_scores = o; o += (size_t)B * p.ld * 4;
+  o = (size_t)round_up((int64_t)o, 256);
+  p.off_topk = o; o += p.tk.bytes;
+  p.off_idx = o; o += (size_t)round_up((int64_t)B * k * 4, 256);
+  p.off_attn = o; o += p.at.bytes;
+  p.bytes = o;
+  return p;
+}
+
+// ---------------------------------------------------------------- launch sequences
+
+dsa_status run_indexer(const dsa_batch* b, const uint8_t* q8, const float* q_scale, const float* w,
+                       const dsa_cache* kidx, const dsa_cache* kscale, int H_I, int d_I, float* scores,
+                       int64_t ld, uint32_t* hist, hipStream_t s) {
+  IndexerArgs a;
+  a.g = make_geo(b);
+  a.kidx = make_cache(kidx);
+  a.ksc = make_cache(kscale);
+  a.q8 = q8;
+  a.q_scale = q_scale;
+  a.w = w;
+  a.scores = scores;
+  a.ld = ld;
+  a.hist = hist;
+  a.H_I = H_I;
+  const bool decode = b->q_start == nullptr;
+  if (decode) {
+    int64_t c = round_up(((int64_t)b->max_len * b->num_seqs + 1023) / 1024, 16);
+    a.chunk = (int)(c < 256 ? 256 : (c > kIdxDecodeChunk ? kIdxDecodeChunk : c));
+    a.ntiles = 1;
+  } else {
+    a.chunk = kIdxPrefillChunk;
+    a.ntiles = (b->max_q + kIdxPrefillRows - 1) / kIdxPrefillRows;
+  }
+  a.nchunks = (b->max_len + a.chunk - 1) / a.chunk;
+  CHECK((int64_t)a.nchunks * a.ntiles < (int64_t)1 << 31, DSA_ERR_UNSUPPORTED, "indexer grid too large");
+  LAUNCH(launch_indexer(a, d_I, decode, hist != nullptr, s), "indexer launch");
+  return DSA_OK;
+}
+
+dsa_status run_topk(const dsa_batch* b, const float* scores, int64_t ld, int k, int32_t* idx,
+                    const TopkPlan& p, char* ws, bool hist_ready, hipStream_t s) {
+  TopkArgs a;
+  a.g = make_geo(b);
+  a.scores = scores;
+  a.ld = ld;
+  a.k = k;
+  a.idx = idx;
+  a.hist = nullptr;
+  a.counters = nullptr;
+  a.slice_cnt = nullptr;
+  a.lists = nullptr;
+  a.slice = p.slice;
+  a.nslices = p.nslices;
+  if (!p.split) {
+    LAUNCH(launch_topk_row(a, s), "top-k launch");
+    return DSA_OK;
+  }
+  a.hist = reinterpret_cast<uint32_t*>(ws + p.off_hist);
+  a.counters = reinterpret_cast<uint32_t*>(ws + p.off_cnt);
+  a.slice_cnt = reinterpret_cast<uint32_t*>(ws + p.off_slice);
+  a.lists = reinterpret_cast<uint2*>(ws + p.off_lists);
+  if (!hist_ready) {
+    LAUNCH(launch_zero(a.hist, (int64_t)p.zero_words, s), "workspace clear");
+    LAUNCH(launch_topk_hist(a, s), "top-k histogram launch");
+  }
+  LAUNCH(launch_topk_split(a, s), "top-k launch");
+  return DSA_OK;
+}
+
+dsa_status run_attn(const dsa_batch* b, const uint16_t* q, const dsa_cache* kv, const dsa_cache* v, int H,
+                    int D, int D_v, float scale, const int32_t* idx, int k, uint16_t* out, float* lse,
+                    const AttnPlan& p, char* ws, hipStream_t s) {
+  AttnArgs a;
+  a.g = make_geo(b);
+  a.kv = make_cache(kv);
+  a.v = make_cache((v && v->data) ? v : nullptr);
+  a.q = q;
+  a.idx = idx;
+  a.k = k;
+  a.H = H;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.out = out;
+  a.lse = lse;
+  a.nsplit = p.nsplit;
+  a.per_split = p.per_split;
+  a.part_o = p.nsplit > 1 ? reinterpret_cast<uint16_t*>(ws + p.off_o) : nullptr;
+  a.part_lse = p.nsplit > 1 ? reinterpret_cast<float*>(ws + p.off_lse) : nullptr;
+  LAUNCH(launch_attn(a, D, D_v, s), "attention launch");
+  if (p.nsplit > 1) {
+    CombineArgs c;
+    c.part_o = a.part_o;
+    c.part_lse = a.part_lse;
+    c.out = out;
+    c.lse = lse;
+    c.T = b->num_rows;
+    c.H = H;
+    c.D_v = D_v;
+    c.nsplit = p.nsplit;
+    LAUNCH(launch_combine(c, s), "attention combine launch");
+  }
+  return DSA_OK;
+}
+
+dsa_status check_indexer_args(const dsa_batch* b, const uint8_t* q8, const float* w, const dsa_cache* kidx,
+                              const dsa_cache* kscale, int H_I, int d_I) {
+  CHECK(q8 && w, DSA_ERR_NULL, "q8 or w is NULL");
+  CHECK(H_I >= 1 && H_I <= 64, DSA_ERR_UNSUPPORTED, "H_I %d outside [1, 64]", H_I);
+  CHECK(d_I == 32 || d_I == 128, DSA_ERR_UNSUPPORTED, "d_I %d not in {32, 128}", d_I);
+  CHECK(aligned(q8, 16), DSA_ERR_ALIGN, "q8 not 16-byte aligned");
+  dsa_status st = check_cache(b, kidx, "index-key", d_I, 16);
+  if (st != DSA_OK) return st;
+  if (kscale && kscale->data) {
+    st = check_cache(b, kscale, "key-scale", 4, 4);
+    if (st != DSA_OK) return st;
+  }
+  return DSA_OK;
+}
+
+dsa_status check_attn_args(const dsa_batch* b, const uint16_t* q, const dsa_cache* kv, const dsa_cache* v, int H,
+                           int D, int D_v, float scale, int k) {
+  CHECK(q, DSA_ERR_NULL, "q is NULL");
+  CHECK((D == 576 && D_v == 512) || (D == 64 && D_v == 64), DSA_ERR_UNSUPPORTED,
+        "(D, D_v) = (%d, %d) not in {(576, 512), (64, 64)}", D, D_v);
+  CHECK(H >= 1 && H <= (D == 64 ? 64 : 128), DSA_ERR_UNSUPPORTED, "H %d outside [1, %d]", H, D == 64 ? 64 : 128);
+  CHECK(k >= 1 && k <= 4096, DSA_ERR_UNSUPPORTED, "k %d outside [1, 4096]", k);
+  CHECK(isfinite(scale), DSA_ERR_SHAPE, "scale is not finite");
+  CHECK(aligned(q, 16), DSA_ERR_ALIGN, "q not 16-byte aligned");
+  dsa_status st = check_cache(b, kv, "kv", (int64_t)D * 2, 16);
+  if (st != DSA_OK) return st;
+  if (v && v->data) {
+    CHECK(D == 64, DSA_ERR_UNSUPPORTED, "a separate V cache is supported for D = 64 only");
+    st = check_cache(b, v, "v", (int64_t)D_v * 2, 16);
+    if (st != DSA_OK) return st;
+  }
+  return DSA_OK;
+}
+
+}  // namespace
+
+// ====================================================================== C ABI
+
+extern "C" const char* dsa_last_error(void) { return g_err.c_str(); }
+
+extern "C" dsa_status dsa_set_stage_events(void* const* events, int count) {
+  if (!events) {
+    g_stage_armed = false;
+    return ok();
+  }
+  CHECK(count >= 4, DSA_ERR_SHAPE, "need 4 stage events, got %d", count);
+  for (int i = 0; i < 4; ++i) {
+    CHECK(events[i], DSA_ERR_NULL, "stage event %d is NULL", i);
+    g_stage_events[i] = static_cast<hipEvent_t>(events[i]);
+  }
+  g_stage_armed = true;
+  return ok();
+}
+
+extern "C" size_t dsa_workspace_size(int entry, const dsa_batch* batch, int k, int H, int D_v) {
+  if (check_batch(batch) != DSA_OK || k < 1 || k > 4096) return (size_t)-1;
+  switch (entry) {
+    case DSA_WS_TOPK:
+      return plan_topk(batch->num_rows, batch->max_len, k).bytes;
+    case DSA_WS_ATTN:
+      if (H < 1 || D_v < 1) return (size_t)-1;
+      return plan_attn(batch->num_rows, k, H, D_v).bytes;
+    case DSA_WS_DECODE:
+      if (H < 1 || D_v < 1 || batch->q_start) return (size_t)-1;
+      return plan_decode(batch->num_seqs, batch->max_len, k, H, D_v).bytes;
+    default:
+      return (size_t)-1;
+  }
+}
+
+extern "C" dsa_status dsa_indexer(const dsa_batch* batch, const uint8_t* q8, const float* q_scale,
+                                  const float* w, const dsa_cache* kidx, const dsa_cache* kscale, int H_I,
+                                  int d_I, float* scores, int64_t ld, void* stream) {
+  dsa_status st = check_batch(batch);
+  if (st != DSA_OK) return st;
+  st = check_indexer_args(batch, q8, w, kidx, kscale, H_I, d_I);
+  if (st != DSA_OK) return st;
+  CHECK(scores, DSA_ERR_NULL, "scores is NULL");
+  CHECK(ld >= batch->max_len, DSA_ERR_SHAPE, "ld %lld < max_len %d", (long long)ld, batch->max_len);
+  if (batch->num_rows == 0) return ok();
+  st = run_indexer(batch, q8, q_scale, w, kidx, kscale, H_I, d_I, scores, ld, nullptr,
+                   static_cast<hipStream_t>(stream));
+  return st == DSA_OK ? ok() : st;
+}
+
+extern "C" dsa_status dsa_topk(const dsa_batch* batch, const float* scores, int64_t ld, int k, int32_t* idx,
+                               void* workspace, size_t ws_bytes, void* stream) {
+  dsa_status st = check_batch(batch);
+  if (st != DSA_OK) return st;
+  CHECK(scores && idx, DSA_ERR_NULL, "scores or idx is NULL");
+  CHECK(k >= 1 && k <= 4096, DSA_ERR_UNSUPPORTED, "k %d outside [1, 4096]", k);
+  CHECK(ld >= batch->max_len, DSA_ERR_SHAPE, "ld %lld < max_len %d", (long long)ld, batch->max_len);
+  CHECK(ld % 4 == 0 && aligned(scores, 16), DSA_ERR_ALIGN, "scores must be 16-byte aligned with ld % 4 == 0");
+  const TopkPlan p = plan_topk(batch->num_rows, batch->max_len, k);
+  if (p.bytes) {
+    CHECK(workspace, DSA_ERR_WORKSPACE, "top-k needs %zu workspace bytes, got NULL", p.bytes);
+    CHECK(ws_bytes >= p.bytes, DSA_ERR_WORKSPACE, "top-k needs %zu workspace bytes, got %zu", p.bytes, ws_bytes);
+    CHECK(aligned(workspace, 256), DSA_ERR_ALIGN, "workspace not 256-byte aligned");
+  }
+  if (batch->num_rows == 0) return ok();
+  st = run_topk(batch, scores, ld, k, idx, p, static_cast<char*>(workspace), false,
+                static_cast<hipStream_t>(stream));
+  return st == DSA_OK ? ok() : st;
+}
+
+extern "C" dsa_status dsa_sparse_attn(const dsa_batch* batch, const uint16_t* q, const dsa_cache* kv,
+                                      const dsa_cache* v, int H, int D, int D_v, float scale, const int32_t* idx,
+                                      int k, uint16_t* out, float* lse, void* workspace, size_t ws_bytes,
+                                      void* stream) {
+  dsa_status st = check_batch(batch);
+  if (st != DSA_OK) return st;
+  st = check_attn_args(batch, q, kv, v, H, D, D_v, scale, k);
+  if (st != DSA_OK) return st;
+  CHECK(idx && out, DSA_ERR_NULL, "idx or out is NULL");
+  const AttnPlan p = plan_attn(batch->num_rows, k, H, D_v);
+  if (p.bytes) {
+    CHECK(workspace, DSA_ERR_WORKSPACE, "attention needs %zu workspace bytes, got NULL", p.bytes);
+    CHECK(ws_bytes >= p.bytes, DSA_ERR_WORKSPACE, "attention needs %zu workspace bytes, got %zu", p.bytes, ws_bytes);
+    CHECK(aligned(workspace, 256), DSA_ERR_ALIGN, "workspace not 256-byte aligned");
+  }
+  if (batch->num_rows == 0) return ok();
+  st = run_attn(batch, q, kv, v, H, D, D_v, scale, idx, k, out, lse, p, static_cast<char*>(workspace),
+                static_cast<hipStream_t>(stream));
+  return st == DSA_OK ? ok() : st;
+}
+
+extern "C" dsa_status dsa_decode(const dsa_batch* batch, const uint8_t* q8, const float* q_scale, const float* w,
+                                 const dsa_cache* kidx, const dsa_cache* kscale, int H_I, int d_I, int k,
+                                 const uint16_t* q, const dsa_cache* kv, const dsa_cache* v, int H, int D, int D_v,
+                                 float scale, uint16_t* out, float* lse, int32_t* idx_out, void* workspace,
+                                 size_t ws_bytes, void* stream) {
+  dsa_status st = check_batch(batch);
+  if (st != DSA_OK) return st;
+  CHECK(batch->q_start == nullptr, DSA_ERR_SHAPE, "dsa_decode takes one query per sequence (q_start must be NULL)");
+  st = check_indexer_args(batch, q8, w, kidx, kscale, H_I, d_I);
+  if (st != DSA_OK) return st;
+  st = check_attn_args(batch, q, kv, v, H, D, D_v, scale, k);
+  if (st != DSA_OK) return st;
+  CHECK(out, DSA_ERR_NULL, "out is NULL");
+  const DecodePlan p = plan_decode(batch->num_seqs, batch->max_len, k, H, D_v);
+  CHECK(workspace, DSA_ERR_WORKSPACE, "decode needs %zu workspace bytes, got NULL", p.bytes);
+  CHECK(ws_bytes >= p.bytes, DSA_ERR_WORKSPACE, "decode needs %zu workspace bytes, got %zu", p.bytes, ws_bytes);
+  CHECK(aligned(workspace, 256), DSA_ERR_ALIGN, "workspace not 256-byte aligned");
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  float* scores = reinterpret_cast<float*>(ws + p.off_scores);
+  char* tws = ws + p.off_topk;
+  int32_t* idx = idx_out ? idx_out : reinterpret_cast<int32_t*>(ws + p.off_idx);
+  const bool timed = g_stage_armed;
+  g_stage_armed = false;
+  auto mark = [&](int i) -> hipError_t { return timed ? hipEventRecord(g_stage_events[i], s) : hipSuccess; };
+  uint32_t* hist = nullptr;
+  if (p.tk.split) {
+    hist = reinterpret_cast<uint32_t*>(tws + p.tk.off_hist);
+    LAUNCH(launch_zero(hist, (int64_t)p.tk.zero_words, s), "workspace clear");
+  }
+  LAUNCH(mark(0), "stage event");
+  st = run_indexer(batch, q8, q_scale, w, kidx, kscale, H_I, d_I, scores, p.ld, hist, s);
+  if (st != DSA_OK) return st;
+  LAUNCH(mark(1), "stage event");
+  st = run_topk(batch, scores, p.ld, k, idx, p.tk, tws, true, s);
+  if (st != DSA_OK) return st;
+  LAUNCH(mark(2), "stage event");
+  st = run_attn(batch, q, kv, v, H, D, D_v, scale, idx, k, out, lse, p.at, ws + p.off_attn, s);
+  if (st != DSA_OK) return st;
+  LAUNCH(mark(3), "stage event");
+  return ok();
+}

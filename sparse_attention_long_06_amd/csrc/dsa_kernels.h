@@ -1,0 +1,92 @@
+// Kernel argument blocks and host launchers of the DSA kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "dsa_common.h"
+
+namespace dsa {
+
+// ---------------------------------------------------------------- indexer
+struct IndexerArgs {
+  Geo g;
+  Cache kidx;            // d_I FP8 bytes per token
+  Cache ksc;             // fp32 per token; data == nullptr means 1
+  const uint8_t* q8;     // [T, H_I, d_I]
+  const float* q_scale;  // [T] or nullptr
+  const float* w;        // [T, H_I]
+  float* scores;         // [T, ld]
+  int64_t ld;
+  uint32_t* hist;        // [T, kBins1] first-pass top-k histogram (decode layout), or nullptr
+  int H_I;
+  int chunk;             // keys per workgroup
+  int nchunks;           // key chunks per row tile
+  int ntiles;            // row tiles per sequence
+};
+
+// Rows of one workgroup in the prefill layout (4 waves x kIdxRowsPerWave rows).
+constexpr int kIdxRowsPerWave = 2;
+constexpr int kIdxPrefillRows = 4 * kIdxRowsPerWave;
+constexpr int kIdxPrefillChunk = 1024;
+constexpr int kIdxDecodeChunk = 4096;
+
+hipError_t launch_indexer(const IndexerArgs& a, int d_I, bool decode_layout, bool with_hist,
+                          hipStream_t stream);
+
+// ---------------------------------------------------------------- top-k
+struct TopkArgs {
+  Geo g;
+  const float* scores;
+  int64_t ld;
+  int k;
+  int32_t* idx;          // [T, k]
+  uint32_t* hist;        // [T, kBins1]           (split mode)
+  uint32_t* counters;    // [T]                   (split mode)
+  uint32_t* slice_cnt;   // [T, nslices]          (split mode)
+  uint2* lists;          // [T, nslices * slice]  (split mode)
+  int slice;             // keys per slice        (split mode)
+  int nslices;
+};
+
+constexpr int kTopkMaxSlices = 64;
+constexpr int kTopkSplitMaxRows = 512;
+
+hipError_t launch_zero(uint32_t* p, int64_t n, hipStream_t stream);
+hipError_t launch_topk_hist(const TopkArgs& a, hipStream_t stream);
+hipError_t launch_topk_split(const TopkArgs& a, hipStream_t stream);
+hipError_t launch_topk_row(const TopkArgs& a, hipStream_t stream);
+
+// ---------------------------------------------------------------- attention
+struct AttnArgs {
+  Geo g;
+  Cache kv;              // D bf16 per token
+  Cache v;               // D_v bf16 per token; data == nullptr: first D_v dims of kv
+  const uint16_t* q;     // [T, H, D]
+  const int32_t* idx;    // [T, k]
+  int k;
+  int H;
+  float scale_log2;      // softmax scale * log2(e)
+  uint16_t* out;         // [T, H, D_v] bf16 (nsplit == 1)
+  float* lse;            // [T, H] or nullptr (nsplit == 1)
+  uint16_t* part_o;      // [T, nsplit, H, D_v] bf16, normalised per split (nsplit > 1)
+  float* part_lse;       // [T, nsplit, H]      (nsplit > 1)
+  int nsplit;
+  int per_split;         // selected slots per split, a multiple of kAttnBlock, <= kAttnMaxSplit
+};
+
+constexpr int kAttnBlock = 64;      // selected rows staged per step
+constexpr int kAttnMaxSplit = 2048; // selected slots one workgroup handles at most
+
+struct CombineArgs {
+  const uint16_t* part_o;
+  const float* part_lse;
+  uint16_t* out;
+  float* lse;
+  int T, H, D_v, nsplit;
+};
+
+hipError_t launch_attn(const AttnArgs& a, int D, int D_v, hipStream_t stream);
+hipError_t launch_combine(const CombineArgs& a, hipStream_t stream);
+
+}  // namespace dsa

@@ -1,0 +1,277 @@
+// Lightning indexer on gfx950: the indexer heads of a query row contracted
+// with a stream of FP8 keys on the matrix cores, ReLU and head-weighted sum
+// fused in registers (ouchyi.pink post on DSA, the DSA paragraph: few heads,
+// FP8; tenelement.pl article "DeepSeek V3.2-Exp Cuts Long-Context Costs with
+// DeepSeek Sparse Attention (DSA) While Maintaining Benchmark Parity",
+// section "Architektura DeepSeek V3.2-Exp: Od MoE do DSA": ReLU logits).
+//
+//   I[t,s] = k_scale[s] * sum_j (w[t,j] * q_scale[t]) * ReLU(q8[t,j] . k8[s])
+//
+// Keys stay FP8 (e4m3fn) in HBM and on the load path; each lane widens its
+// fragment in registers with v_cvt_scalef32_pk_bf16_fp8 (exact: every e4m3fn
+// value is a bf16 value) and the contraction runs on
+// v_mfma_f32_16x16x32_bf16.  The FP8 MFMA forms were measured to sum their
+// products in a window of about 20 bits below the largest product (error up
+// to 1.4e-5 of sum|q_d k_d|), which moves scores near the top-k threshold by
+// ~1e-4 relative; the bf16 form accumulates to fp32 rounding.  Decode is
+// HBM-bound, so the wider MFMA costs no time there.
+//
+// MFMA mapping: M = indexer heads (16 per tile), N = 16 keys, K = 32 dims per
+// instruction, d_I/32 instructions chained through the accumulator.  Lane l
+// holds key (l % 16) and heads 4*(l/16)+i of each tile, so the head sum is
+// 4*HT in-lane FMAs plus two cross-lane adds.  The contraction index is split
+// over the four 16-lane groups the same way for both operands (group g holds
+// bytes [g*d_I/4, (g+1)*d_I/4) of a row; instruction c takes 8 of them),
+// which is all a dot product needs.
+//
+// Two layouts share the kernel:
+//   decode  (one query row per sequence): the 4 waves of a workgroup split a
+//           chunk of keys; key bytes are streamed once with non-temporal
+//           loads; optionally the kernel also builds the first-pass top-k
+//           histogram (high 11 bits of the order key) of its row.
+//   prefill (many rows per sequence): each wave owns kIdxRowsPerWave rows
+//           and walks the whole key chunk, so each key tile feeds
+//           HT*d_I/32*kIdxRowsPerWave MFMAs; key chunks past the tile's last
+//           position are skipped (causality).
+#include "dsa_common.h"
+#include "dsa_kernels.h"
+
+namespace dsa {
+
+// Raw FP8 fragment of one row held by a lane: d_I/4 bytes.
+template <int DI> struct Frag;
+template <> struct Frag<128> { v4i lo, hi; };
+template <> struct Frag<32> { long v; };
+
+template <int DI, bool NT>
+__device__ __forceinline__ void load_frag(Frag<DI>& f, const char* row, int grp) {
+  if constexpr (DI == 128) {
+    const v4i* p = reinterpret_cast<const v4i*>(row + 32 * grp);
+    if constexpr (NT) {
+      f.lo = __builtin_nontemporal_load(p);
+      f.hi = __builtin_nontemporal_load(p + 1);
+    } else {
+      f.lo = p[0];
+      f.hi = p[1];
+    }
+  } else {
+    const long* p = reinterpret_cast<const long*>(row + 8 * grp);
+    if constexpr (NT) f.v = __builtin_nontemporal_load(p); else f.v = *p;
+  }
+}
+
+template <int DI>
+__device__ __forceinline__ void zero_frag(Frag<DI>& f) {
+  if constexpr (DI == 128) {
+    f.lo = v4i{0, 0, 0, 0};
+    f.hi = v4i{0, 0, 0, 0};
+  } else {
+    f.v = 0;
+  }
+}
+
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+
+// Eight e4m3fn bytes (two dwords) -> eight bf16, exactly.
+__device__ __forceinline__ v8bf widen8(int lo, int hi) {
+  const v2bf a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false);
+  const v2bf b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true);
+  const v2bf c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false);
+  const v2bf d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true);
+  return v8bf{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
+// bf16 view of a fragment: d_I/32 chunks of 8 values.
+template <int DI> struct Wide { v8bf c[DI / 32]; };
+
+template <int DI>
+__device__ __forceinline__ Wide<DI> widen(const Frag<DI>& f) {
+  Wide<DI> w;
+  if constexpr (DI == 128) {
+    w.c[0] = widen8(f.lo.x, f.lo.y);
+    w.c[1] = widen8(f.lo.z, f.lo.w);
+    w.c[2] = widen8(f.hi.x, f.hi.y);
+    w.c[3] = widen8(f.hi.z, f.hi.w);
+  } else {
+    w.c[0] = widen8((int)(f.v & 0xFFFFFFFF), (int)(f.v >> 32));
+  }
+  return w;
+}
+
+template <int DI>
+__device__ __forceinline__ v4f mfma_dot(const Wide<DI>& a, const Wide<DI>& b) {
+  v4f acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int c = 0; c < DI / 32; ++c) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.c[c], b.c[c], acc, 0, 0, 0);
+  return acc;
+}
+
+template <int HT, int DI, int R, int RW, bool HIST>
+__global__ void __launch_bounds__(256) indexer_kernel(IndexerArgs a) {
+  constexpr int KW = 4 / RW;            // waves sharing one row group (they split the keys)
+  constexpr bool STREAM = (RW == 1);    // decode: every key byte is read exactly once
+  constexpr int U = (R == 1) ? 4 : 2;   // key tiles per pipeline stage
+  static_assert(!HIST || (R == 1 && RW == 1), "histogram needs one row per workgroup");
+  __shared__ uint32_t hist[HIST ? kBins1 : 1];
+
+  const int b = blockIdx.z;
+  const int ytile = blockIdx.x % a.ntiles;
+  const int chunk_id = blockIdx.x / a.ntiles;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int nl = lane & 15, grp = lane >> 4;
+  const int rg = wave / KW, kw = wave % KW;
+
+  const int len = a.g.seq_lens[b];
+  int row0, nq;
+  if (a.g.q_start) {
+    row0 = a.g.q_start[b];
+    nq = a.g.q_start[b + 1] - row0;
+  } else {
+    row0 = b;
+    nq = 1;
+  }
+  const int tile_r0 = ytile * (RW * R);
+  if (tile_r0 >= nq) return;
+  const int base_pos = len - nq;                      // position of the sequence's first query row
+  const int last_r = min(tile_r0 + RW * R, nq) - 1;
+  const int kbeg = chunk_id * a.chunk;
+  const int kend = min(kbeg + a.chunk, base_pos + last_r + 1);
+  if (kbeg >= kend) return;                           // uniform over the workgroup
+
+  if constexpr (HIST) {
+    for (int i = threadIdx.x; i < kBins1; i += 256) hist[i] = 0u;
+    __syncthreads();
+  }
+
+  // ---- this wave's query rows: widened A operands and folded head weights in registers
+  Wide<DI> qa[R][HT];
+  float wq[R][HT][4];
+  int nrow[R];
+  int64_t trow[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int ri = tile_r0 + rg * R + r;
+    const bool ok = ri < nq;
+    nrow[r] = ok ? base_pos + ri + 1 : 0;
+    const int t = row0 + (ok ? ri : 0);
+    trow[r] = t;
+    const float qs = a.q_scale ? a.q_scale[t] : 1.0f;
+#pragma unroll
+    for (int ht = 0; ht < HT; ++ht) {
+      const int h = ht * 16 + nl;
+      Frag<DI> raw;
+      if (ok && h < a.H_I)
+        load_frag<DI, false>(raw, reinterpret_cast<const char*>(a.q8) + ((int64_t)t * a.H_I + h) * DI, grp);
+      else
+        zero_frag<DI>(raw);
+      qa[r][ht] = widen<DI>(raw);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int hw = ht * 16 + grp * 4 + i;
+        wq[r][ht][i] = (ok && hw < a.H_I) ? a.w[(int64_t)t * a.H_I + hw] * qs : 0.0f;
+      }
+    }
+  }
+
+  // ---- key tiles of 16 keys; this wave takes tiles kw, kw+KW, ...
+  const int ntiles = (kend - kbeg + 15) >> 4;
+  const int my_tiles = ntiles > kw ? (ntiles - kw + KW - 1) / KW : 0;
+
+  auto load_stage = [&](Frag<DI> (&kt)[U], float (&ks)[U], int m0) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (m0 + u < my_tiles) {
+        const int s = kbeg + ((kw + KW * (m0 + u)) << 4) + nl;
+        const int sl = min(s, kend - 1);
+        load_frag<DI, STREAM>(kt[u], token_ptr(a.g, a.kidx, b, sl), grp);
+        ks[u] = a.ksc.data ? *reinterpret_cast<const float*>(token_ptr(a.g, a.ksc, b, sl)) : 1.0f;
+      }
+    }
+  };
+
+  auto compute_stage = [&](const Frag<DI> (&kt)[U], const float (&ks)[U], int m0) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (m0 + u < my_tiles) {
+        const int s0 = kbeg + ((kw + KW * (m0 + u)) << 4);
+        const Wide<DI> kb = widen<DI>(kt[u]);
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          if (s0 < nrow[r]) {                         // wave-uniform causal skip
+            float part = 0.0f;
+#pragma unroll
+            for (int ht = 0; ht < HT; ++ht) {
+              const v4f acc = mfma_dot<DI>(qa[r][ht], kb);
+              part = fmaf(wq[r][ht][0], fmaxf(acc[0], 0.0f), part);
+              part = fmaf(wq[r][ht][1], fmaxf(acc[1], 0.0f), part);
+              part = fmaf(wq[r][ht][2], fmaxf(acc[2], 0.0f), part);
+              part = fmaf(wq[r][ht][3], fmaxf(acc[3], 0.0f), part);
+            }
+            part += __shfl_xor(part, 16);
+            part += __shfl_xor(part, 32);
+            const int s = s0 + nl;
+            if (grp == 0 && s < nrow[r]) {
+              const float sc = part * ks[u];
+              a.scores[trow[r] * a.ld + s] = sc;
+              if constexpr (HIST) atomicAdd(&hist[score_key(sc) >> (32 - kBins1Bits)], 1u);
+            }
+          }
+        }
+      }
+    }
+  };
+
+  Frag<DI> bufA[U], bufB[U];
+  float ksA[U], ksB[U];
+  load_stage(bufA, ksA, 0);
+  for (int m0 = 0; m0 < my_tiles; m0 += 2 * U) {
+    if (m0 + U < my_tiles) load_stage(bufB, ksB, m0 + U);
+    compute_stage(bufA, ksA, m0);
+    if (m0 + U >= my_tiles) break;
+    if (m0 + 2 * U < my_tiles) load_stage(bufA, ksA, m0 + 2 * U);
+    compute_stage(bufB, ksB, m0 + U);
+  }
+
+  if constexpr (HIST) {
+    __syncthreads();
+    uint32_t* gh = a.hist + (int64_t)row0 * kBins1;
+    for (int i = threadIdx.x; i < kBins1; i += 256) {
+      const uint32_t c = hist[i];
+      if (c) atomicAdd(gh + i, c);
+    }
+  }
+}
+
+template <int HT, int DI>
+static hipError_t launch_ht(const IndexerArgs& a, bool decode_layout, bool with_hist, hipStream_t s) {
+  const dim3 grid(a.nchunks * a.ntiles, 1, a.g.num_seqs);
+  if (decode_layout) {
+    if (with_hist)
+      hipLaunchKernelGGL((indexer_kernel<HT, DI, 1, 1, true>), grid, dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL((indexer_kernel<HT, DI, 1, 1, false>), grid, dim3(256), 0, s, a);
+  } else {
+    hipLaunchKernelGGL((indexer_kernel<HT, DI, kIdxRowsPerWave, 4, false>), grid, dim3(256), 0, s, a);
+  }
+  return hipGetLastError();
+}
+
+template <int DI>
+static hipError_t launch_di(const IndexerArgs& a, bool decode_layout, bool with_hist, hipStream_t s) {
+  switch ((a.H_I + 15) / 16) {
+    case 1: return launch_ht<1, DI>(a, decode_layout, with_hist, s);
+    case 2: return launch_ht<2, DI>(a, decode_layout, with_hist, s);
+    case 3: return launch_ht<3, DI>(a, decode_layout, with_hist, s);
+    case 4: return launch_ht<4, DI>(a, decode_layout, with_hist, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_indexer(const IndexerArgs& a, int d_I, bool decode_layout, bool with_hist,
+                          hipStream_t stream) {
+  if (d_I == 128) return launch_di<128>(a, decode_layout, with_hist, stream);
+  if (d_I == 32) return launch_di<32>(a, decode_layout, with_hist, stream);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace dsa

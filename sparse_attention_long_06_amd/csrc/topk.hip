@@ -1,0 +1,404 @@
+// Per-row top-k selection on gfx950 (ouchyi.pink post on DSA, the DSA
+// paragraph: a fixed budget of tokens per query; digitalreport.com.tr article
+// "DeepSeek V3.2-exp: daha ucuz uzun bağlamlı AI": fine-grained token
+// selection; sider.ai "Sparse attention that isn't sparse thinking", section
+// "Matematik, Minimalist Sürüm": selection has to be vectorised and
+// cache-aware to pay off).
+//
+// Order: score descending, then token index ascending; -0.0 ties +0.0.  The
+// result is the ascending list of the first min(k, n) tokens in that order,
+// padded with -1.
+//
+// Method: radix select on an order-preserving 32-bit key (11 + 11 + 10 bits).
+// Each pass histograms the keys that share the prefix found so far (LDS
+// atomics), and a block scan over the bins finds the bin holding the k-th
+// key.  The final pass is an ordered compaction: per 4-element thread chunks,
+// one block scan of packed (greater, equal) counts gives every kept token its
+// output slot, so indices come out ascending and ties at the threshold go to
+// the lowest indices.  A pass stops refining as soon as the whole boundary
+// bin is needed.
+//
+// Two kernels:
+//   row mode   one workgroup per row; after the first pass the candidates
+//              (keys at or above the boundary bin) are compacted into LDS and
+//              the remaining passes run there.
+//   split mode for a few long rows (decode): S workgroups per row each
+//              compact their slice's candidates into global memory, using the
+//              row histogram that the indexer (or topk_hist_kernel) built;
+//              the last workgroup to finish (an atomic ticket after a release
+//              fence) finishes the selection for the row.
+#include "dsa_common.h"
+#include "dsa_kernels.h"
+
+namespace dsa {
+
+struct BinSel {
+  uint32_t bin, above, cnt;
+};
+
+// ---- element sources: size() and load4(i, ...) for i a multiple of 4
+
+struct RowSrc {  // fp32 scores in global memory; token index = base + i
+  const float* p;
+  int n;
+  int base;
+  __device__ int size() const { return n; }
+  __device__ void load4(int i, uint32_t (&key)[4], int (&id)[4], bool (&ok)[4]) const {
+    if (i + 3 < n && ((reinterpret_cast<uintptr_t>(p + i) & 15) == 0)) {
+      const float4 v = *reinterpret_cast<const float4*>(p + i);
+      key[0] = score_key(v.x); key[1] = score_key(v.y);
+      key[2] = score_key(v.z); key[3] = score_key(v.w);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) { id[j] = base + i + j; ok[j] = true; }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        ok[j] = i + j < n;
+        key[j] = ok[j] ? score_key(p[i + j]) : 0u;
+        id[j] = base + i + j;
+      }
+    }
+  }
+};
+
+struct LdsSrc {  // (key, index) pairs in LDS
+  const uint32_t* key;
+  const int* id;
+  int n;
+  __device__ int size() const { return n; }
+  __device__ void load4(int i, uint32_t (&k)[4], int (&d)[4], bool (&ok)[4]) const {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      ok[j] = i + j < n;
+      k[j] = ok[j] ? key[i + j] : 0u;
+      d[j] = ok[j] ? id[i + j] : -1;
+    }
+  }
+};
+
+struct SegSrc {  // per-slice (key, index) lists in global memory, concatenated in slice order
+  const uint2* lists;   // slice s starts at lists + s * slice
+  const uint32_t* offs; // LDS [nslices + 1] prefix of the slice counts
+  int nslices;
+  int slice;
+  __device__ int size() const { return (int)offs[nslices]; }
+  __device__ void load4(int i, uint32_t (&k)[4], int (&d)[4], bool (&ok)[4]) const {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t pos = (uint32_t)(i + j);
+      ok[j] = pos < offs[nslices];
+      k[j] = 0u;
+      d[j] = -1;
+      if (ok[j]) {
+        int lo = 0, hi = nslices - 1;  // last slice with offs[s] <= pos
+        while (lo < hi) {
+          const int mid = (lo + hi + 1) >> 1;
+          if (offs[mid] <= pos) lo = mid; else hi = mid - 1;
+        }
+        const uint2 e = lists[(int64_t)lo * slice + (pos - offs[lo])];
+        k[j] = e.x;
+        d[j] = (int)e.y;
+      }
+    }
+  }
+};
+
+// ---- block-level building blocks (every thread of the block calls them)
+
+// Histogram of bits [shift, shift+bits) of the keys whose top `pbits` bits equal P.
+template <int NT, class Src>
+__device__ void hist_pass(const Src& src, uint32_t* hist, uint32_t P, int pbits, int shift, int bits) {
+  const int nb = 1 << bits;
+  for (int i = threadIdx.x; i < nb; i += NT) hist[i] = 0u;
+  __syncthreads();
+  const uint32_t mask = (uint32_t)nb - 1u;
+  const int n = src.size();
+  for (int i = threadIdx.x * 4; i < n; i += NT * 4) {
+    uint32_t key[4];
+    int id[4];
+    bool ok[4];
+    src.load4(i, key, id, ok);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (ok[j] && (pbits == 0 || (key[j] >> (32 - pbits)) == P))
+        atomicAdd(&hist[(key[j] >> shift) & mask], 1u);
+    }
+  }
+  __syncthreads();
+}
+
+// The bin (scanning from the top) where the running count reaches `need`,
+// how many keys lie in higher bins, and how many are in the bin.
+template <int NT>
+__device__ BinSel select_bin(const uint32_t* hist, int nb, uint32_t need, uint32_t* tmp, BinSel* res) {
+  const int per = (nb + NT - 1) / NT;
+  uint32_t c = 0;
+  for (int j = 0; j < per; ++j) {
+    const int d = threadIdx.x * per + j;
+    if (d < nb) c += hist[nb - 1 - d];
+  }
+  uint32_t tot;
+  const uint32_t pre = block_exclusive_scan<NT>(c, tmp, tot);
+  if (pre < need && need <= pre + c) {
+    uint32_t run = pre;
+    for (int j = 0; j < per; ++j) {
+      const int d = threadIdx.x * per + j;
+      if (d >= nb) break;
+      const uint32_t h = hist[nb - 1 - d];
+      if (run + h >= need) {
+        res->bin = (uint32_t)(nb - 1 - d);
+        res->above = run;
+        res->cnt = h;
+        break;
+      }
+      run += h;
+    }
+  }
+  __syncthreads();
+  const BinSel r = *res;
+  __syncthreads();
+  return r;
+}
+
+// Ordered compaction: in ascending source order, emit every element whose
+// top-`pbits` key prefix is greater than P plus the first `need_eq` whose
+// prefix equals P; emit(slot, key, index) gets consecutive slots.  Stops once
+// `target` elements are out.  Returns the number emitted (uniform).
+template <int NT, class Src, class Emit>
+__device__ uint32_t compact(const Src& src, uint32_t P, int pbits, uint32_t need_eq, uint32_t target,
+                           uint32_t* tmp, Emit emit) {
+  const int shift = 32 - pbits;
+  uint32_t gt_base = 0, eq_base = 0;
+  const int n = src.size();
+  for (int base = 0; base < n; base += NT * 4) {
+    uint32_t key[4];
+    int id[4];
+    bool ok[4];
+    src.load4(base + threadIdx.x * 4, key, id, ok);
+    uint32_t fgt = 0, feq = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (ok[j]) {
+        const uint32_t pre = key[j] >> shift;
+        if (pre > P) fgt |= 1u << j;
+        else if (pre == P) feq |= 1u << j;
+      }
+    }
+    const uint32_t packed = (uint32_t)__popc(fgt) | ((uint32_t)__popc(feq) << 16);
+    uint32_t tot;
+    const uint32_t ex = block_exclusive_scan<NT>(packed, tmp, tot);
+    uint32_t gt = gt_base + (ex & 0xFFFFu), eq = eq_base + (ex >> 16);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if ((fgt >> j) & 1u) {
+        emit(gt + min(eq, need_eq), key[j], id[j]);
+        ++gt;
+      } else if ((feq >> j) & 1u) {
+        if (eq < need_eq) emit(gt + eq, key[j], id[j]);
+        ++eq;
+      }
+    }
+    gt_base += tot & 0xFFFFu;
+    eq_base += tot >> 16;
+    if (gt_base + min(eq_base, need_eq) >= target) break;
+  }
+  return gt_base + min(eq_base, need_eq);
+}
+
+// Refine (P, pbits) until the boundary bin is needed whole or the key is
+// exhausted, then emit the selection in source order.
+template <int NT, class Src, class Emit>
+__device__ void refine_and_emit(const Src& src, uint32_t P, int pbits, uint32_t need, uint32_t cnt,
+                                uint32_t* hist, uint32_t* tmp, BinSel* res, uint32_t target, Emit emit) {
+  while (cnt != need && pbits < 32) {
+    const int bits = (pbits + 11 <= 22) ? 11 : 32 - pbits;
+    const int shift = 32 - pbits - bits;
+    hist_pass<NT>(src, hist, P, pbits, shift, bits);
+    const BinSel s = select_bin<NT>(hist, 1 << bits, need, tmp, res);
+    P = (P << bits) | s.bin;
+    pbits += bits;
+    need -= s.above;
+    cnt = s.cnt;
+  }
+  compact<NT>(src, P, pbits, need, target, tmp, emit);
+}
+
+__device__ __forceinline__ void write_identity(int32_t* out, int n, int k, int tid, int nt) {
+  for (int i = tid; i < k; i += nt) out[i] = i < n ? i : -1;
+}
+
+// ---------------------------------------------------------------- row mode
+
+constexpr int kRowNT = 512;
+constexpr int kRowCap = 8192;
+
+__global__ void __launch_bounds__(kRowNT) topk_row_kernel(TopkArgs a) {
+  __shared__ uint32_t hist[kBins1];
+  __shared__ uint32_t tmp[kRowNT / 64];
+  __shared__ BinSel res;
+  __shared__ uint32_t lkey[kRowCap];
+  __shared__ int lidx[kRowCap];
+
+  const int t = blockIdx.x;
+  int b, pos;
+  row_seq_pos(a.g, t, b, pos);
+  const int n = pos + 1;
+  int32_t* out = a.idx + (int64_t)t * a.k;
+  const uint32_t k = (uint32_t)a.k;
+  if (n <= a.k) {
+    write_identity(out, n, a.k, threadIdx.x, kRowNT);
+    return;
+  }
+  const RowSrc row{a.scores + (int64_t)t * a.ld, n, 0};
+  auto to_out = [&](uint32_t slot, uint32_t, int id) { out[slot] = id; };
+
+  hist_pass<kRowNT>(row, hist, 0u, 0, 32 - kBins1Bits, kBins1Bits);
+  const BinSel s1 = select_bin<kRowNT>(hist, kBins1, k, tmp, &res);
+  const uint32_t need = k - s1.above;
+  if (s1.cnt == need) {
+    compact<kRowNT>(row, s1.bin, kBins1Bits, need, k, tmp, to_out);
+    return;
+  }
+  const uint32_t m = s1.above + s1.cnt;
+  if (m <= (uint32_t)kRowCap) {
+    compact<kRowNT>(row, s1.bin, kBins1Bits, s1.cnt, m, tmp,
+                    [&](uint32_t slot, uint32_t key, int id) { lkey[slot] = key; lidx[slot] = id; });
+    __syncthreads();
+    const LdsSrc ls{lkey, lidx, (int)m};
+    refine_and_emit<kRowNT>(ls, s1.bin, kBins1Bits, need, s1.cnt, hist, tmp, &res, k, to_out);
+  } else {
+    refine_and_emit<kRowNT>(row, s1.bin, kBins1Bits, need, s1.cnt, hist, tmp, &res, k, to_out);
+  }
+}
+
+// ---------------------------------------------------------------- split mode
+
+constexpr int kSplitNT = 256;
+constexpr int kSplitCap = 8192;
+
+__global__ void __launch_bounds__(kSplitNT) topk_hist_kernel(TopkArgs a) {
+  __shared__ uint32_t hist[kBins1];
+  const int sl = blockIdx.x, t = blockIdx.y;
+  int b, pos;
+  row_seq_pos(a.g, t, b, pos);
+  const int n = pos + 1;
+  if (n <= a.k) return;
+  const int beg = sl * a.slice, end = min(n, beg + a.slice);
+  if (beg >= end) return;
+  const RowSrc src{a.scores + (int64_t)t * a.ld + beg, end - beg, beg};
+  hist_pass<kSplitNT>(src, hist, 0u, 0, 32 - kBins1Bits, kBins1Bits);
+  uint32_t* gh = a.hist + (int64_t)t * kBins1;
+  for (int i = threadIdx.x; i < kBins1; i += kSplitNT) {
+    const uint32_t c = hist[i];
+    if (c) atomicAdd(gh + i, c);
+  }
+}
+
+__global__ void __launch_bounds__(kSplitNT) topk_split_kernel(TopkArgs a) {
+  __shared__ uint32_t hist[kBins1];
+  __shared__ uint32_t tmp[kSplitNT / 64];
+  __shared__ BinSel res;
+  __shared__ uint32_t lkey[kSplitCap];
+  __shared__ int lidx[kSplitCap];
+  __shared__ uint32_t offs[kTopkMaxSlices + 1];
+  __shared__ uint32_t is_last;
+
+  const int sl = blockIdx.x, t = blockIdx.y;
+  int b, pos;
+  row_seq_pos(a.g, t, b, pos);
+  const int n = pos + 1;
+  const uint32_t k = (uint32_t)a.k;
+  int32_t* out = a.idx + (int64_t)t * a.k;
+  if (n <= a.k) {
+    if (sl == 0) write_identity(out, n, a.k, threadIdx.x, kSplitNT);
+    return;
+  }
+
+  // first pass: the row histogram is complete (built by an earlier launch)
+  const uint32_t* gh = a.hist + (int64_t)t * kBins1;
+  for (int i = threadIdx.x; i < kBins1; i += kSplitNT) hist[i] = gh[i];
+  __syncthreads();
+  const BinSel s1 = select_bin<kSplitNT>(hist, kBins1, k, tmp, &res);
+
+  // this slice's candidates (keys in the boundary bin or above), in index order
+  const int beg = sl * a.slice, end = min(n, beg + a.slice);
+  uint2* mylist = a.lists + ((int64_t)t * a.nslices + sl) * a.slice;
+  uint32_t mycnt = 0;
+  if (beg < end) {
+    const RowSrc src{a.scores + (int64_t)t * a.ld + beg, end - beg, beg};
+    mycnt = compact<kSplitNT>(src, s1.bin, kBins1Bits, 0xFFFFFFFFu, 0xFFFFFFFFu, tmp,
+                              [&](uint32_t slot, uint32_t key, int id) {
+                                mylist[slot] = make_uint2(key, (uint32_t)id);
+                              });
+  }
+  if (threadIdx.x == 0) a.slice_cnt[(int64_t)t * a.nslices + sl] = mycnt;
+
+  // ticket: the last slice of the row to arrive finishes the selection
+  __threadfence();
+  __syncthreads();
+  if (threadIdx.x == 0) is_last = (atomicAdd(&a.counters[t], 1u) == (uint32_t)(a.nslices - 1)) ? 1u : 0u;
+  __syncthreads();
+  if (!is_last) return;
+  __threadfence();
+
+  if (threadIdx.x == 0) {
+    uint32_t o = 0;
+    for (int s = 0; s < a.nslices; ++s) {
+      offs[s] = o;
+      o += __atomic_load_n(&a.slice_cnt[(int64_t)t * a.nslices + s], __ATOMIC_RELAXED);
+    }
+    offs[a.nslices] = o;
+  }
+  __syncthreads();
+  const uint32_t m = offs[a.nslices];
+  const uint32_t need = k - s1.above;
+  auto to_out = [&](uint32_t slot, uint32_t, int id) { out[slot] = id; };
+  const uint2* rowlists = a.lists + (int64_t)t * a.nslices * a.slice;
+  if (m <= (uint32_t)kSplitCap) {
+    for (int s = 0; s < a.nslices; ++s) {
+      const uint32_t c = offs[s + 1] - offs[s];
+      const uint2* src = rowlists + (int64_t)s * a.slice;
+      for (uint32_t i = threadIdx.x; i < c; i += kSplitNT) {
+        const uint2 e = src[i];
+        lkey[offs[s] + i] = e.x;
+        lidx[offs[s] + i] = (int)e.y;
+      }
+    }
+    __syncthreads();
+    const LdsSrc ls{lkey, lidx, (int)m};
+    refine_and_emit<kSplitNT>(ls, s1.bin, kBins1Bits, need, s1.cnt, hist, tmp, &res, k, to_out);
+  } else {
+    const SegSrc gs{rowlists, offs, a.nslices, a.slice};
+    refine_and_emit<kSplitNT>(gs, s1.bin, kBins1Bits, need, s1.cnt, hist, tmp, &res, k, to_out);
+  }
+}
+
+__global__ void zero_u32_kernel(uint32_t* p, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+    p[i] = 0u;
+}
+
+hipError_t launch_zero(uint32_t* p, int64_t n, hipStream_t stream) {
+  if (n <= 0) return hipSuccess;
+  const int64_t want = (n + 255) / 256;
+  const int64_t blocks = want < 1024 ? want : 1024;
+  hipLaunchKernelGGL(zero_u32_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, p, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_topk_hist(const TopkArgs& a, hipStream_t stream) {
+  hipLaunchKernelGGL(topk_hist_kernel, dim3(a.nslices, a.g.num_rows), dim3(kSplitNT), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_topk_split(const TopkArgs& a, hipStream_t stream) {
+  hipLaunchKernelGGL(topk_split_kernel, dim3(a.nslices, a.g.num_rows), dim3(kSplitNT), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_topk_row(const TopkArgs& a, hipStream_t stream) {
+  hipLaunchKernelGGL(topk_row_kernel, dim3(a.g.num_rows), dim3(kRowNT), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace dsa

@@ -1,0 +1,227 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle on the same seeded inputs.
+
+Rules (see tests/gpu_helpers.py): integer-exact inputs must give bit-exact
+scores and indices; otherwise scores within 1e-4 of their absolute-term
+scale, top-k swaps only among near-ties of the k-th score (bit-exact when
+both sides select from the same fp32 scores), attention within
+2e-2 + 1e-2*|ref|.  No oracle input comes from the HIP path.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+import sparse_attention_long_06_amd as dsa
+from tests.gpu_helpers import (DEV, announce, arrays_of, check_attention, check_scores, check_topk_swaps,
+                               gpu_staged, oracle_abs_terms, to_np)
+
+pytestmark = pytest.mark.gpu
+
+
+# ------------------------------------------------------------------ tiny prefill (integer-exact indexer)
+
+def test_tiny_prefill_bit_exact_selection_and_attention():
+    wl = W.TINY_PREFILL
+    announce("tiny_prefill_L256 staged", wl)
+    inp = W.generate(wl, "cpu")
+    scores, idx, out, lse = gpu_staged(inp.to(DEV))
+    scores, idx, out, lse = to_np(scores), to_np(idx), to_np(out), to_np(lse)
+
+    a = arrays_of(inp)
+    rows = list(range(wl.seq_len))
+    ref = oracle.run_rows(a, rows)
+    for r in rows:
+        assert np.array_equal(scores[r, : r + 1].astype(np.float64), ref["scores"][r]), f"scores row {r}"
+        assert np.array_equal(idx[r], ref["idx"][r]), f"top-k row {r}"
+        check_attention(out[r], lse[r], ref["out"][r], ref["lse"][r], f"row {r}")
+    # against the fp32 originals the bf16 rounding of q/k/v is the only difference
+    ref32 = oracle.run_rows(arrays_of(inp, use_fp32_originals=True), rows[::17])
+    for i, r in enumerate(rows[::17]):
+        check_attention(out[r], None, ref32["out"][i], None, f"fp32 originals row {r}")
+
+
+# ------------------------------------------------------------------ production shapes, small contexts
+
+SMALL = [W.SMALL_DECODE, W.SMALL_PAGED, W.SMALL_PREFILL]
+
+
+def _rows_for(inp):
+    if inp.wl.kind == "decode":
+        return list(range(inp.num_rows))
+    return W.sample_rows(inp.wl, inp.num_rows, 160,
+                         always=(0, 1, 2, 2046, 2047, 2048, 2049, inp.num_rows - 1))
+
+
+@pytest.mark.parametrize("wl", SMALL, ids=[w.name for w in SMALL])
+def test_small_end_to_end(wl):
+    announce("end-to-end", wl.name)
+    inp = W.generate(wl, DEV)
+    scores, idx, out, lse = gpu_staged(inp)
+    scores, idx, out, lse = to_np(scores), to_np(idx), to_np(out), to_np(lse)
+    a = arrays_of(inp)
+    rows = _rows_for(inp)
+    ref = oracle.run_rows(a, rows)
+    absterms = oracle_abs_terms(a, rows)
+    check_scores(scores, ref["scores"], absterms, rows)
+    same = 0
+    for i, r in enumerate(rows):
+        if check_topk_swaps(idx[r], ref["idx"][i], ref["scores"][i], wl.k):
+            same += 1
+            check_attention(out[r], lse[r], ref["out"][i], ref["lse"][i], f"{wl.name} row {r}")
+    assert same >= 0.9 * len(rows), f"only {same}/{len(rows)} rows selected the same set"
+
+
+def test_small_chunked_prefill():
+    wl = W.SMALL_CHUNKED
+    first = W.generate(wl, DEV, chunk_index=0)
+    cache = W.cache_of(first)
+    nchunks = (wl.seq_len + wl.chunk - 1) // wl.chunk
+    for c in range(nchunks):
+        announce("chunked prefill", wl.name, "chunk", c)
+        inp = first if c == 0 else W.generate(wl, DEV, chunk_index=c, cache=cache)
+        scores, idx, out, lse = (to_np(x) for x in gpu_staged(inp))
+        a = arrays_of(inp)
+        rows = W.sample_rows(wl, inp.num_rows, 40, always=(0, inp.num_rows - 1))
+        ref = oracle.run_rows(a, rows)
+        check_scores(scores, ref["scores"], oracle_abs_terms(a, rows), rows)
+        for i, r in enumerate(rows):
+            if check_topk_swaps(idx[r], ref["idx"][i], ref["scores"][i], wl.k):
+                check_attention(out[r], lse[r], ref["out"][i], ref["lse"][i], f"chunk {c} row {r}")
+
+
+# ------------------------------------------------------------------ attention stage on the oracle's index sets
+
+@pytest.mark.parametrize("wl", [W.SMALL_DECODE, W.SMALL_PAGED, W.SMALL_PREFILL], ids=lambda w: w.name)
+def test_attention_stage_on_oracle_indices(wl):
+    announce("attention stage", wl.name)
+    inp = W.generate(wl, DEV)
+    a = arrays_of(inp)
+    rows = list(range(inp.num_rows)) if inp.num_rows <= 16 else W.sample_rows(wl, inp.num_rows, 64, always=(0, 2047, inp.num_rows - 1))
+    ref = oracle.run_rows(a, rows)
+    idx_full = np.full((inp.num_rows, wl.k), -1, dtype=np.int32)
+    for i, r in enumerate(rows):
+        idx_full[r] = ref["idx"][i]
+    batch = dsa.Batch.from_inputs(inp)
+    out, lse = dsa.sparse_attn(batch, inp.q, inp.kv, inp.v, wl.scale, torch.from_numpy(idx_full).to(DEV),
+                               D_v=wl.D_v)
+    out, lse = to_np(out), to_np(lse)
+    for i, r in enumerate(rows):
+        check_attention(out[r], lse[r], ref["out"][i], ref["lse"][i], f"{wl.name} row {r}")
+    # rows given no index at all: zero output, lse = -inf
+    empty = [r for r in range(inp.num_rows) if r not in set(rows)][:3]
+    for r in empty:
+        assert np.all(out[r] == 0) and np.all(np.isneginf(lse[r]))
+
+
+def test_attention_ragged_and_padded_index_sets():
+    # index sets shorter than k (-1 padded), unsorted, and a single token
+    wl = W.SMALL_DECODE
+    announce("attention ragged sets", wl.name)
+    inp = W.generate(wl, DEV)
+    a = arrays_of(inp)
+    rng = np.random.default_rng(5)
+    idx = np.full((inp.num_rows, wl.k), -1, dtype=np.int32)
+    sets = []
+    for r, L in enumerate(inp.seq_lens_host):
+        m = [1, 777, 2048][r % 3]
+        s = rng.choice(L, size=m, replace=False).astype(np.int32)
+        idx[r, rng.permutation(wl.k)[:m]] = s
+        sets.append(np.sort(s))
+    batch = dsa.Batch.from_inputs(inp)
+    out, lse = dsa.sparse_attn(batch, inp.q, inp.kv, inp.v, wl.scale, torch.from_numpy(idx).to(DEV), D_v=wl.D_v)
+    out, lse = to_np(out), to_np(lse)
+    for r, s in enumerate(sets):
+        K = oracle.decode_bf16(a["kv"][r, s])
+        ro, rl = oracle.sparse_attention(oracle.decode_bf16(a["q"][r]), K, K[:, : wl.D_v], wl.scale)
+        check_attention(out[r], lse[r], ro, rl, f"row {r} m={len(s)}")
+
+
+# ------------------------------------------------------------------ top-k kernel on shared fp32 scores (bit-exact)
+
+def _decode_batch(lens):
+    t = torch.tensor(lens, dtype=torch.int32, device=DEV)
+    return dsa.Batch(seq_lens=t, num_rows=len(lens), max_q=1, max_len=max(lens))
+
+
+def _prefill_batch(L):
+    return dsa.Batch(seq_lens=torch.tensor([L], dtype=torch.int32, device=DEV), num_rows=L, max_q=L, max_len=L,
+                     q_start=torch.tensor([0, L], dtype=torch.int32, device=DEV))
+
+
+def _check_topk_rows(scores, lens_of_row, k, idx):
+    s = scores.cpu().numpy()
+    g = idx.cpu().numpy()
+    for r, n in enumerate(lens_of_row):
+        ref = oracle.topk_indices(s[r, :n], k)
+        assert np.array_equal(g[r], ref), f"row {r} (n={n}, k={k}): first diff at {np.argmax(g[r] != ref)}"
+
+
+@pytest.mark.parametrize("kind", ["normal", "ties", "signed_zeros", "all_equal", "sparse_ones"])
+@pytest.mark.parametrize("k", [1, 64, 2048, 4096])
+def test_topk_split_mode_bit_exact(kind, k):
+    announce("topk split mode", kind, k)
+    lens = [100, 2048, 2049, 5000, 20000, 33333, 4096 + 1, 9000]
+    batch = _decode_batch(lens)
+    scores = W.synthetic_scores(len(lens), (max(lens) + 3) // 4 * 4, kind, seed=k, device=DEV)
+    idx = dsa.topk(batch, scores, k)
+    torch.cuda.synchronize()
+    _check_topk_rows(scores, lens, k, idx)
+
+
+@pytest.mark.parametrize("kind", ["normal", "ties", "signed_zeros", "sparse_ones"])
+def test_topk_row_mode_bit_exact(kind):
+    announce("topk row mode", kind)
+    L = 3000
+    batch = _prefill_batch(L)
+    scores = W.synthetic_scores(L, L, kind, seed=7, device=DEV)
+    idx = dsa.topk(batch, scores, 2048)
+    torch.cuda.synchronize()
+    _check_topk_rows(scores, [r + 1 for r in range(L)], 2048, idx)
+
+
+@pytest.mark.parametrize("kind", ["all_equal", "sparse_ones", "normal"])
+def test_topk_row_mode_long_rows(kind):
+    # > 512 rows of up to 20000 candidates: row mode, including the path where
+    # the boundary bin overflows the LDS candidate buffer
+    announce("topk row mode long rows", kind)
+    lens = [20000 - 17 * i for i in range(600)]
+    batch = _decode_batch(lens)
+    scores = W.synthetic_scores(len(lens), 20000, kind, seed=3, device=DEV)
+    idx = dsa.topk(batch, scores, 2048)
+    torch.cuda.synchronize()
+    _check_topk_rows(scores, lens, 2048, idx)
+
+
+# ------------------------------------------------------------------ fused decode
+
+@pytest.mark.parametrize("wl", [W.SMALL_DECODE, W.SMALL_PAGED], ids=lambda w: w.name)
+def test_fused_decode_matches_staged_bitwise(wl):
+    announce("fused decode vs staged", wl.name)
+    inp = W.generate(wl, DEV)
+    scores, idx_s, out_s, lse_s = gpu_staged(inp)
+    batch = dsa.Batch.from_inputs(inp)
+    idx_f = torch.empty_like(idx_s)
+    out_f, lse_f, _ = dsa.decode(batch, inp.q8, inp.q_scale, inp.w, inp.k8, inp.k_scale, wl.k, inp.q, inp.kv,
+                                 inp.v, wl.scale, idx_out=idx_f, D_v=wl.D_v)
+    out_g, lse_g, _ = dsa.decode(batch, inp.q8, inp.q_scale, inp.w, inp.k8, inp.k_scale, wl.k, inp.q, inp.kv,
+                                 inp.v, wl.scale, D_v=wl.D_v)
+    torch.cuda.synchronize()
+    assert torch.equal(idx_f, idx_s)
+    assert torch.equal(out_f.view(torch.int16), out_s.view(torch.int16))
+    assert torch.equal(lse_f, lse_s)
+    # a second fused call (no index output) is bit-identical too: no races, no float atomics
+    assert torch.equal(out_g.view(torch.int16), out_f.view(torch.int16))
+    assert torch.equal(lse_g, lse_f)
+
+
+def test_binding_reports_bad_arguments():
+    wl = W.SMALL_DECODE
+    announce("binding error path")
+    inp = W.generate(wl, DEV)
+    batch = dsa.Batch.from_inputs(inp)
+    bad_q8 = torch.zeros((inp.num_rows, 64, 64), dtype=torch.uint8, device=DEV)   # d_I = 64: no kernel
+    with pytest.raises(dsa.DsaError, match="DSA_ERR_UNSUPPORTED"):
+        dsa.indexer(batch, bad_q8, inp.q_scale, inp.w, inp.k8, inp.k_scale)
+    with pytest.raises(ValueError):
+        dsa.topk(batch, torch.zeros((inp.num_rows, 5000), device=DEV), 5000)   # k > 4096

@@ -5,4 +5,4 @@ Holds shapes, seeds and random draws only; no part of the method is computed her
 from .configs import (ALL, BY_NAME, CHUNKED_128K, DECODE_128K, PAGED_DECODE_MIXED,  # noqa: F401
                       PREFILL_32K, SMALL_CHUNKED, SMALL_DECODE, SMALL_PAGED, SMALL_PREFILL,
                       TINY_PREFILL, Workload)
-from .gen import Inputs, cache_of, generate, quantize_e4m3fn, sample_rows  # noqa: F401
+from .gen import Inputs, cache_of, generate, quantize_e4m3fn, sample_rows, synthetic_scores  # noqa: F401

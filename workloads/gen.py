@@ -29,6 +29,7 @@ CPU device gives different, equally valid values.
 """
 from __future__ import annotations
 
+import dataclasses
 import math
 import zlib
 from dataclasses import dataclass
@@ -98,6 +99,15 @@ class Inputs:
     @property
     def paged(self) -> bool:
         return self.block_table is not None
+
+    def to(self, device) -> "Inputs":
+        """A copy with every tensor moved to ``device``."""
+        moved = {}
+        for f in dataclasses.fields(self):
+            v = getattr(self, f.name)
+            moved[f.name] = v.to(device) if isinstance(v, torch.Tensor) else v
+        moved["device"] = torch.device(device)
+        return Inputs(**moved)
 
     def row_positions(self):
         """(sequence, position) of every query row, host lists."""
@@ -274,3 +284,31 @@ def sample_rows(wl: Workload, num_rows: int, count: int, always=()) -> list:
             out.append(r)
             seen.add(r)
     return sorted(out)
+
+
+def synthetic_scores(rows: int, ld: int, kind: str, seed: int = 0, device="cpu") -> torch.Tensor:
+    """Seeded fp32 score matrices [rows, ld] that stress the top-k selection.
+
+    normal: N(0,1); ties: integers in [-3,3]; signed_zeros: +0.0 / -0.0 with a
+    few +-1; all_equal: every score 0.5; sparse_ones: zeros with about 1000
+    ones per row (the boundary is a huge run of equal zeros).
+    """
+    dev = torch.device(device)
+    gd = dev.type if dev.type == "cpu" else dev
+    g = _gen(gd, seed, "scores_" + kind, rows * 7 + ld)
+    if kind == "normal":
+        return torch.randn((rows, ld), generator=g, device=dev)
+    if kind == "ties":
+        return torch.randint(-3, 4, (rows, ld), generator=g, device=dev).float()
+    if kind == "signed_zeros":
+        v = torch.randint(0, 16, (rows, ld), generator=g, device=dev)
+        out = torch.zeros((rows, ld), device=dev)
+        out = torch.where(v < 7, torch.full_like(out, -0.0), out)
+        out = torch.where(v == 14, torch.ones_like(out), out)
+        out = torch.where(v == 15, -torch.ones_like(out), out)
+        return out
+    if kind == "all_equal":
+        return torch.full((rows, ld), 0.5, device=dev)
+    if kind == "sparse_ones":
+        return (torch.rand((rows, ld), generator=g, device=dev) < (1000.0 / ld)).float()
+    raise ValueError(kind)
