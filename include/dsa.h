@@ -93,12 +93,12 @@ typedef struct dsa_batch {
  * DSA": logits per context token with a ReLU).
  *   q8      [T, H_I, d_I] e4m3fn, row-major
  *   q_scale [T] fp32 per-token dequantisation scale, or NULL (= 1)
- *   w       [T, H_I] fp32 head weights
+ *   w       [T, H_I] fp32 head weights, 16-byte aligned
  *   kidx    d_I e4m3fn bytes per token; data and row_stride 16-byte aligned
  *   kscale  one fp32 per token (row_stride >= 4), or NULL (= 1)
  *   scores  [T, ld] fp32 out: scores[t*ld + s] for s <= p_t; entries past
  *           p_t are unspecified.  ld >= max_len.
- * Supported: 1 <= H_I <= 64, d_I in {32, 128}.
+ * Supported: H_I a multiple of 4 in [4, 64], d_I in {32, 128}.
  */
 dsa_status dsa_indexer(const dsa_batch* batch, const uint8_t* q8, const float* q_scale,
                        const float* w, const dsa_cache* kidx, const dsa_cache* kscale,

@@ -107,8 +107,8 @@ Cache make_cache(const dsa_cache* c) {
 struct TopkPlan {
   bool split = false;
   int nslices = 0, slice = 0;
-  size_t off_hist = 0, off_cnt = 0, off_slice = 0, off_lists = 0, bytes = 0;
-  size_t zero_words = 0;  // hist + counters + slice counts, contiguous from off_hist
+  size_t off_hist = 0, off_slice = 0, off_lists = 0, bytes = 0;
+  size_t zero_words = 0;  // the histograms, from off_hist
 };
 
 TopkPlan plan_topk(int T, int max_len, int k) {
@@ -127,9 +127,8 @@ TopkPlan plan_topk(int T, int max_len, int k) {
   p.nslices = ns;
   size_t o = 0;
   p.off_hist = o; o += (size_t)T * kBins1 * 4;
-  p.off_cnt = o; o += (size_t)T * 4;
-  p.off_slice = o; o += (size_t)T * ns * 4;
   p.zero_words = o / 4;
+  p.off_slice = o; o += (size_t)T * ns * 4;
   o = (size_t)round_up((int64_t)o, 256);
   p.off_lists = o; o += (size_t)T * ns * slice * 8;
   p.bytes = (size_t)round_up((int64_t)o, 256);
@@ -226,7 +225,6 @@ dsa_status run_topk(const dsa_batch* b, const float* scores, int64_t ld, int k, 
   a.k = k;
   a.idx = idx;
   a.hist = nullptr;
-  a.counters = nullptr;
   a.slice_cnt = nullptr;
   a.lists = nullptr;
   a.slice = p.slice;
@@ -236,7 +234,6 @@ dsa_status run_topk(const dsa_batch* b, const float* scores, int64_t ld, int k, 
     return DSA_OK;
   }
   a.hist = reinterpret_cast<uint32_t*>(ws + p.off_hist);
-  a.counters = reinterpret_cast<uint32_t*>(ws + p.off_cnt);
   a.slice_cnt = reinterpret_cast<uint32_t*>(ws + p.off_slice);
   a.lists = reinterpret_cast<uint2*>(ws + p.off_lists);
   if (!hist_ready) {
@@ -284,7 +281,8 @@ dsa_status run_attn(const dsa_batch* b, const uint16_t* q, const dsa_cache* kv, 
 dsa_status check_indexer_args(const dsa_batch* b, const uint8_t* q8, const float* w, const dsa_cache* kidx,
                               const dsa_cache* kscale, int H_I, int d_I) {
   CHECK(q8 && w, DSA_ERR_NULL, "q8 or w is NULL");
-  CHECK(H_I >= 1 && H_I <= 64, DSA_ERR_UNSUPPORTED, "H_I %d outside [1, 64]", H_I);
+  CHECK(H_I >= 4 && H_I <= 64 && H_I % 4 == 0, DSA_ERR_UNSUPPORTED, "H_I %d not a multiple of 4 in [4, 64]", H_I);
+  CHECK(aligned(w, 16), DSA_ERR_ALIGN, "w not 16-byte aligned");
   CHECK(d_I == 32 || d_I == 128, DSA_ERR_UNSUPPORTED, "d_I %d not in {32, 128}", d_I);
   CHECK(aligned(q8, 16), DSA_ERR_ALIGN, "q8 not 16-byte aligned");
   dsa_status st = check_cache(b, kidx, "index-key", d_I, 16);

@@ -38,20 +38,31 @@ typedef __attribute__((address_space(3))) v4s lds_v4s;
 
 __device__ __forceinline__ int swz(int r) { return (r >> 1) & 7; }
 
+// s_waitcnt immediate for "vmcnt(0)" on gfx9-family parts: vmcnt bits [3:0]
+// and [15:14] zero, expcnt [6:4] and lgkmcnt [11:8] at their maximum.
+constexpr int kWaitVmcnt0 = 0x0F70;
+
 // Issue the gather of one block of kAttnBlock rows (CH chunks each) into `tile`.
 // Every wave issues its share of 64-chunk DMA instructions; invalid rows read a
 // valid stand-in row (their weight is zero, their values only need be finite).
+// The DMA is written as inline asm on purpose: the compiler would otherwise
+// make the first LDS read after it wait for it (it cannot tell the two tiles
+// apart), which would serialise the double buffering.  Completion is ordered
+// explicitly with s_waitcnt vmcnt(0) + a barrier before a tile is read.
 template <int CH>
 __device__ __forceinline__ void gather_block(char* tile, const char* base, int64_t row_stride,
                                              const uint32_t* rowid, int waves, int wave, int lane) {
   constexpr int RB = kAttnBlock;
   constexpr int NI = RB * CH / 64;                 // DMA instructions per block
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)tile;
   for (int ins = wave; ins < NI; ins += waves) {
     const int p = ins * 64 + lane;                 // chunk position in the tile
     const int r = p / CH, pc = p % CH;
     const int c = pc ^ swz(r);
     const char* src = base + (int64_t)rowid[r] * row_stride + c * 16;
-    __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(tile + ins * 64 * 16), 16, 0, 0);
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds0 + ins * 64 * 16);
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+                 :: "s"(m0), "v"(src) : "memory");
   }
 }
 
@@ -146,22 +157,13 @@ __global__ void __launch_bounds__(512) attn_kernel(AttnArgs a) {
     for (int u = 0; u < 4; ++u) vbase[u] = (rv * CHV + ((2 * u + ((nl & 3) >> 1)) ^ yv)) * 16 + (nl & 1) * 8;
   }
 
-  if (nblocks > 0) {
-    gather_block<CH>(ktile[0], a.kv.data, a.kv.row_stride, rowid, waves, wave, lane);
-    if constexpr (SEPV) gather_block<CHV>(vtile[0], a.v.data, a.v.row_stride, vrowid, waves, wave, lane);
-  }
+  auto gather = [&](char* kdst, char* vdst, int blk) {
+    gather_block<CH>(kdst, a.kv.data, a.kv.row_stride, rowid + blk * RB, waves, wave, lane);
+    if constexpr (SEPV) gather_block<CHV>(vdst, a.v.data, a.v.row_stride, vrowid + blk * RB, waves, wave, lane);
+  };
 
-  for (int blk = 0; blk < nblocks; ++blk) {
-    const int cur = blk & 1;
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();   // block blk is in LDS; nobody reads the other buffer any more
-    if (blk + 1 < nblocks) {
-      gather_block<CH>(ktile[cur ^ 1], a.kv.data, a.kv.row_stride, rowid + (blk + 1) * RB, waves, wave, lane);
-      if constexpr (SEPV)
-        gather_block<CHV>(vtile[cur ^ 1], a.v.data, a.v.row_stride, vrowid + (blk + 1) * RB, waves, wave, lane);
-    }
-    const char* kt = ktile[cur];
-    const char* vt = SEPV ? vtile[cur] : ktile[cur];
+  auto compute = [&](const char* kt, const char* vtv, int blk) {
+    const char* vt = SEPV ? vtv : kt;
     const uint8_t* vld = valid + blk * RB;
 
     // ---- S^T = K q^T: each K fragment read from LDS feeds HW head tiles.
@@ -258,6 +260,17 @@ __global__ void __launch_bounds__(512) attn_kernel(AttnArgs a) {
           o[ht][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pf[ht][kb], vf[kb], o[ht][nt], 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
     }
+  };
+
+  if (nblocks > 0) gather(ktile[0], vtile[0], 0);
+  for (int blk = 0; blk < nblocks; ++blk) {
+    const int cur = blk & 1;
+    // vmcnt(0) (expcnt/lgkmcnt untouched), as a builtin so the compiler's own
+    // wait tracking sees it too
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    __syncthreads();   // block blk is in LDS; nobody reads the other buffer any more
+    if (blk + 1 < nblocks) gather(ktile[cur ^ 1], vtile[cur ^ 1], blk + 1);
+    compute(ktile[cur], vtile[cur], blk);
   }
 
   // ---- finish: full denominator per head, normalise, write

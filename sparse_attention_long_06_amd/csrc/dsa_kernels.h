@@ -42,7 +42,6 @@ struct TopkArgs {
   int k;
   int32_t* idx;          // [T, k]
   uint32_t* hist;        // [T, kBins1]           (split mode)
-  uint32_t* counters;    // [T]                   (split mode)
   uint32_t* slice_cnt;   // [T, nslices]          (split mode)
   uint2* lists;          // [T, nslices * slice]  (split mode)
   int slice;             // keys per slice        (split mode)

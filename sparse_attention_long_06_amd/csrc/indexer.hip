@@ -165,11 +165,13 @@ __global__ void __launch_bounds__(256) indexer_kernel(IndexerArgs a) {
       else
         zero_frag<DI>(raw);
       qa[r][ht] = widen<DI>(raw);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int hw = ht * 16 + grp * 4 + i;
-        wq[r][ht][i] = (ok && hw < a.H_I) ? a.w[(int64_t)t * a.H_I + hw] * qs : 0.0f;
-      }
+      const int hw = ht * 16 + grp * 4;
+      const float4 w4 = (ok && hw < a.H_I) ? *reinterpret_cast<const float4*>(a.w + (int64_t)t * a.H_I + hw)
+                                           : make_float4(0.f, 0.f, 0.f, 0.f);
+      wq[r][ht][0] = w4.x * qs;
+      wq[r][ht][1] = w4.y * qs;
+      wq[r][ht][2] = w4.z * qs;
+      wq[r][ht][3] = w4.w * qs;
     }
   }
 
@@ -242,10 +244,175 @@ __global__ void __launch_bounds__(256) indexer_kernel(IndexerArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Decode indexer with an LDS ring per wave (d_I = 128).
+//
+// Each wave streams its own 16-key tiles through a ring of kRing slots in
+// LDS.  Tiles arrive by global_load_lds DMA: every 1 KB instruction covers 8
+// whole keys, so HBM reads are fully coalesced, and up to kRing-1 tiles
+// (about 14 KB per wave) are in flight with no registers held for them.
+// Inside a slot, the 16-byte chunk c of key n sits at chunk c ^ ((n>>1)&7),
+// which keeps the 16 lanes of an MFMA operand read on distinct banks.
+// The DMA is inline asm and its completion is awaited with explicit
+// s_waitcnt vmcnt(N): DMA transfers are loads and complete in issue order, so
+// "at most (kRing-1)*PER memory ops outstanding" means the oldest tile landed.
+constexpr int kRing = 8;
+
+__device__ __forceinline__ int kswz(int n) { return (n >> 1) & 7; }
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
+}
+
+template <int HT, bool HIST, bool SCALE>
+__global__ void __launch_bounds__(256) indexer_decode_ring_kernel(IndexerArgs a) {
+  constexpr int DI = 128;
+  constexpr int SLOT = 16 * DI + 64;          // key bytes + 16 fp32 scales
+  constexpr int PER = SCALE ? 3 : 2;          // DMA instructions per tile
+  __shared__ uint32_t hist[HIST ? kBins1 : 1];
+  __shared__ __attribute__((aligned(16))) char ring[4][kRing][SLOT];
+
+  const int b = blockIdx.z;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int nl = lane & 15, grp = lane >> 4;
+
+  const int len = a.g.seq_lens[b];
+  const int kbeg = blockIdx.x * a.chunk;
+  const int kend = min(kbeg + a.chunk, len);
+  if (kbeg >= kend) return;                   // uniform over the workgroup
+  if constexpr (HIST) {
+    for (int i = threadIdx.x; i < kBins1; i += 256) hist[i] = 0u;
+  }
+
+  // query row b: widened A operands and folded head weights in registers
+  Wide<DI> qa[HT];
+  float wq[HT][4];
+  {
+    const float qs = a.q_scale ? a.q_scale[b] : 1.0f;
+#pragma unroll
+    for (int ht = 0; ht < HT; ++ht) {
+      const int h = ht * 16 + nl;
+      Frag<DI> raw;
+      if (h < a.H_I)
+        load_frag<DI, false>(raw, reinterpret_cast<const char*>(a.q8) + ((int64_t)b * a.H_I + h) * DI, grp);
+      else
+        zero_frag<DI>(raw);
+      qa[ht] = widen<DI>(raw);
+      // heads ht*16+4*grp .. +3 (H_I is a multiple of 4, rows 16-byte aligned)
+      const int hw = ht * 16 + grp * 4;
+      const float4 w4 = hw < a.H_I ? *reinterpret_cast<const float4*>(a.w + (int64_t)b * a.H_I + hw)
+                                   : make_float4(0.f, 0.f, 0.f, 0.f);
+      wq[ht][0] = w4.x * qs;
+      wq[ht][1] = w4.y * qs;
+      wq[ht][2] = w4.z * qs;
+      wq[ht][3] = w4.w * qs;
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0x0F70);         // operands are in; the ring owns vmcnt from here
+  if constexpr (HIST) __syncthreads();
+
+  const int ntiles = (kend - kbeg + 15) >> 4;
+  const int my_tiles = ntiles > wave ? (ntiles - wave + 3) / 4 : 0;   // tiles wave, wave+4, ...
+  char* myring = &ring[wave][0][0];
+  const uint32_t ring_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)myring;
+
+  // A 16-key tile never straddles a page (pages hold a power-of-two >= 16
+  // tokens and tiles start at multiples of 16), so its keys are consecutive
+  // token rows starting at the row of its first key.  That row is computed
+  // from wave-uniform values, so any page-table read is a scalar load and
+  // does not disturb the vector-memory counter the ring relies on.
+  auto tile_row0 = [&](int s0) -> int64_t {
+    const int su = __builtin_amdgcn_readfirstlane(s0);
+    if (a.g.block_table) {
+      // constant address space: the table is read-only here, so this is an s_load
+      const auto* tbl = (const __attribute__((address_space(4))) int32_t*)(uintptr_t)a.g.block_table;
+      const int blk = tbl[(int64_t)b * a.g.max_blocks + (su >> a.g.block_shift)];
+      return ((int64_t)blk << a.g.block_shift) + (su & ((1 << a.g.block_shift) - 1));
+    }
+    return (int64_t)b * a.kidx.seq_stride + su;
+  };
+
+  auto issue = [&](int m) {                   // DMA of this wave's m-th tile into slot m % kRing
+    const int s0 = kbeg + ((wave + 4 * m) << 4);
+    const int last = kend - 1 - s0;           // keys past the end re-read the last key
+    const int64_t row0 = tile_row0(s0);
+    const uint32_t slot = ring_lds + (uint32_t)((m % kRing) * SLOT);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int p = i * 64 + lane;            // chunk position in the slot
+      const int n = p >> 3, pc = p & 7;
+      const char* src = a.kidx.data + (row0 + min(n, last)) * a.kidx.row_stride + 16 * (pc ^ kswz(n));
+      const uint32_t m0 = __builtin_amdgcn_readfirstlane(slot + i * 1024);
+      asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" :: "s"(m0), "v"(src) : "memory");
+    }
+    if constexpr (SCALE) {
+      const char* src = a.ksc.data + (row0 + min(lane, last)) * a.ksc.row_stride;
+      const uint32_t m0 = __builtin_amdgcn_readfirstlane(slot + 16 * DI);
+      if (lane < 16)
+        asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off" :: "s"(m0), "v"(src) : "memory");
+    }
+  };
+
+  for (int m = 0; m < kRing - 1 && m < my_tiles; ++m) issue(m);
+
+  const int rb0 = nl * DI + 16 * ((2 * grp) ^ kswz(nl));
+  const int rb1 = nl * DI + 16 * ((2 * grp + 1) ^ kswz(nl));
+  for (int m = 0; m < my_tiles; ++m) {
+    if (m + kRing - 1 < my_tiles) {
+      issue(m + kRing - 1);
+      wait_vmcnt<(kRing - 1) * PER>();
+    } else {
+      wait_vmcnt<0>();
+    }
+    const char* slot = myring + (m % kRing) * SLOT;
+    Frag<DI> kf;
+    kf.lo = *reinterpret_cast<const v4i*>(slot + rb0);
+    kf.hi = *reinterpret_cast<const v4i*>(slot + rb1);
+    const float ks = SCALE ? *reinterpret_cast<const float*>(slot + 16 * DI + 4 * nl) : 1.0f;
+    const Wide<DI> kb = widen<DI>(kf);
+    float part = 0.0f;
+#pragma unroll
+    for (int ht = 0; ht < HT; ++ht) {
+      const v4f acc = mfma_dot<DI>(qa[ht], kb);
+      part = fmaf(wq[ht][0], fmaxf(acc[0], 0.0f), part);
+      part = fmaf(wq[ht][1], fmaxf(acc[1], 0.0f), part);
+      part = fmaf(wq[ht][2], fmaxf(acc[2], 0.0f), part);
+      part = fmaf(wq[ht][3], fmaxf(acc[3], 0.0f), part);
+    }
+    part += __shfl_xor(part, 16);
+    part += __shfl_xor(part, 32);
+    const int s = kbeg + ((wave + 4 * m) << 4) + nl;
+    if (grp == 0 && s < kend) {
+      const float sc = part * ks;
+      a.scores[(int64_t)b * a.ld + s] = sc;
+      if constexpr (HIST) atomicAdd(&hist[score_key(sc) >> (32 - kBins1Bits)], 1u);
+    }
+  }
+
+  if constexpr (HIST) {
+    __syncthreads();
+    uint32_t* gh = a.hist + (int64_t)b * kBins1;
+    for (int i = threadIdx.x; i < kBins1; i += 256) {
+      const uint32_t c = hist[i];
+      if (c) atomicAdd(gh + i, c);
+    }
+  }
+}
+
 template <int HT, int DI>
 static hipError_t launch_ht(const IndexerArgs& a, bool decode_layout, bool with_hist, hipStream_t s) {
   const dim3 grid(a.nchunks * a.ntiles, 1, a.g.num_seqs);
-  if (decode_layout) {
+  if (decode_layout && DI == 128) {
+    const bool sc = a.ksc.data != nullptr;
+    if (with_hist) {
+      if (sc) hipLaunchKernelGGL((indexer_decode_ring_kernel<HT, true, true>), grid, dim3(256), 0, s, a);
+      else hipLaunchKernelGGL((indexer_decode_ring_kernel<HT, true, false>), grid, dim3(256), 0, s, a);
+    } else {
+      if (sc) hipLaunchKernelGGL((indexer_decode_ring_kernel<HT, false, true>), grid, dim3(256), 0, s, a);
+      else hipLaunchKernelGGL((indexer_decode_ring_kernel<HT, false, false>), grid, dim3(256), 0, s, a);
+    }
+  } else if (decode_layout) {
     if (with_hist)
       hipLaunchKernelGGL((indexer_kernel<HT, DI, 1, 1, true>), grid, dim3(256), 0, s, a);
     else

@@ -10,6 +10,8 @@
 // padded with -1.
 //
 // Method: radix select on an order-preserving 32-bit key (11 + 11 + 10 bits).
+// Every pass over memory issues kUnr chunks of loads per thread before
+// consuming any, so a pass costs about one memory latency, not one per chunk.
 // Each pass histograms the keys that share the prefix found so far (LDS
 // atomics), and a block scan over the bins finds the bin holding the k-th
 // key.  The final pass is an ordered compaction: per 4-element thread chunks,
@@ -25,8 +27,9 @@
 //   split mode for a few long rows (decode): S workgroups per row each
 //              compact their slice's candidates into global memory, using the
 //              row histogram that the indexer (or topk_hist_kernel) built;
-//              the last workgroup to finish (an atomic ticket after a release
-//              fence) finishes the selection for the row.
+//              a second launch, one workgroup per row, concatenates the lists
+//              and finishes the selection (the launch boundary orders the
+//              memory, with no fences or tickets inside a kernel).
 #include "dsa_common.h"
 #include "dsa_kernels.h"
 
@@ -105,6 +108,10 @@ struct SegSrc {  // per-slice (key, index) lists in global memory, concatenated 
 
 // ---- block-level building blocks (every thread of the block calls them)
 
+// Chunks of NT*4 elements whose loads are issued together before any of
+// them is consumed: global sources are latency-bound otherwise.
+constexpr int kUnr = 8;
+
 // Histogram of bits [shift, shift+bits) of the keys whose top `pbits` bits equal P.
 template <int NT, class Src>
 __device__ void hist_pass(const Src& src, uint32_t* hist, uint32_t P, int pbits, int shift, int bits) {
@@ -113,16 +120,18 @@ __device__ void hist_pass(const Src& src, uint32_t* hist, uint32_t P, int pbits,
   __syncthreads();
   const uint32_t mask = (uint32_t)nb - 1u;
   const int n = src.size();
-  for (int i = threadIdx.x * 4; i < n; i += NT * 4) {
-    uint32_t key[4];
-    int id[4];
-    bool ok[4];
-    src.load4(i, key, id, ok);
+  for (int base = 0; base < n; base += NT * 4 * kUnr) {
+    uint32_t key[kUnr][4];
+    int id[kUnr][4];
+    bool ok[kUnr][4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      if (ok[j] && (pbits == 0 || (key[j] >> (32 - pbits)) == P))
-        atomicAdd(&hist[(key[j] >> shift) & mask], 1u);
-    }
+    for (int u = 0; u < kUnr; ++u) src.load4(base + (u * NT + threadIdx.x) * 4, key[u], id[u], ok[u]);
+#pragma unroll
+    for (int u = 0; u < kUnr; ++u)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (ok[u][j] && (pbits == 0 || (key[u][j] >> (32 - pbits)) == P))
+          atomicAdd(&hist[(key[u][j] >> shift) & mask], 1u);
   }
   __syncthreads();
 }
@@ -170,37 +179,42 @@ __device__ uint32_t compact(const Src& src, uint32_t P, int pbits, uint32_t need
   const int shift = 32 - pbits;
   uint32_t gt_base = 0, eq_base = 0;
   const int n = src.size();
-  for (int base = 0; base < n; base += NT * 4) {
-    uint32_t key[4];
-    int id[4];
-    bool ok[4];
-    src.load4(base + threadIdx.x * 4, key, id, ok);
-    uint32_t fgt = 0, feq = 0;
+  for (int base = 0; base < n; base += NT * 4 * kUnr) {
+    uint32_t key[kUnr][4];
+    int id[kUnr][4];
+    bool ok[kUnr][4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      if (ok[j]) {
-        const uint32_t pre = key[j] >> shift;
-        if (pre > P) fgt |= 1u << j;
-        else if (pre == P) feq |= 1u << j;
-      }
-    }
-    const uint32_t packed = (uint32_t)__popc(fgt) | ((uint32_t)__popc(feq) << 16);
-    uint32_t tot;
-    const uint32_t ex = block_exclusive_scan<NT>(packed, tmp, tot);
-    uint32_t gt = gt_base + (ex & 0xFFFFu), eq = eq_base + (ex >> 16);
+    for (int u = 0; u < kUnr; ++u) src.load4(base + (u * NT + threadIdx.x) * 4, key[u], id[u], ok[u]);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      if ((fgt >> j) & 1u) {
-        emit(gt + min(eq, need_eq), key[j], id[j]);
-        ++gt;
-      } else if ((feq >> j) & 1u) {
-        if (eq < need_eq) emit(gt + eq, key[j], id[j]);
-        ++eq;
+    for (int u = 0; u < kUnr; ++u) {
+      if (base + u * NT * 4 >= n) break;              // uniform
+      uint32_t fgt = 0, feq = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (ok[u][j]) {
+          const uint32_t pre = key[u][j] >> shift;
+          if (pre > P) fgt |= 1u << j;
+          else if (pre == P) feq |= 1u << j;
+        }
       }
+      const uint32_t packed = (uint32_t)__popc(fgt) | ((uint32_t)__popc(feq) << 16);
+      uint32_t tot;
+      const uint32_t ex = block_exclusive_scan<NT>(packed, tmp, tot);
+      uint32_t gt = gt_base + (ex & 0xFFFFu), eq = eq_base + (ex >> 16);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if ((fgt >> j) & 1u) {
+          emit(gt + min(eq, need_eq), key[u][j], id[u][j]);
+          ++gt;
+        } else if ((feq >> j) & 1u) {
+          if (eq < need_eq) emit(gt + eq, key[u][j], id[u][j]);
+          ++eq;
+        }
+      }
+      gt_base += tot & 0xFFFFu;
+      eq_base += tot >> 16;
+      if (gt_base + min(eq_base, need_eq) >= target) return gt_base + min(eq_base, need_eq);
     }
-    gt_base += tot & 0xFFFFu;
-    eq_base += tot >> 16;
-    if (gt_base + min(eq_base, need_eq) >= target) break;
   }
   return gt_base + min(eq_base, need_eq);
 }
@@ -274,6 +288,7 @@ __global__ void __launch_bounds__(kRowNT) topk_row_kernel(TopkArgs a) {
 // ---------------------------------------------------------------- split mode
 
 constexpr int kSplitNT = 256;
+constexpr int kFinalNT = 512;
 constexpr int kSplitCap = 8192;
 
 __global__ void __launch_bounds__(kSplitNT) topk_hist_kernel(TopkArgs a) {
@@ -294,33 +309,28 @@ __global__ void __launch_bounds__(kSplitNT) topk_hist_kernel(TopkArgs a) {
   }
 }
 
-__global__ void __launch_bounds__(kSplitNT) topk_split_kernel(TopkArgs a) {
+// Phase 1 of split mode: each slice compacts its candidates (keys in the
+// first-pass boundary bin or above, read off the complete row histogram) into
+// its own list region, in index order, and records how many it wrote.
+__global__ void __launch_bounds__(kSplitNT) topk_slice_kernel(TopkArgs a) {
   __shared__ uint32_t hist[kBins1];
   __shared__ uint32_t tmp[kSplitNT / 64];
   __shared__ BinSel res;
-  __shared__ uint32_t lkey[kSplitCap];
-  __shared__ int lidx[kSplitCap];
-  __shared__ uint32_t offs[kTopkMaxSlices + 1];
-  __shared__ uint32_t is_last;
 
   const int sl = blockIdx.x, t = blockIdx.y;
   int b, pos;
   row_seq_pos(a.g, t, b, pos);
   const int n = pos + 1;
   const uint32_t k = (uint32_t)a.k;
-  int32_t* out = a.idx + (int64_t)t * a.k;
   if (n <= a.k) {
-    if (sl == 0) write_identity(out, n, a.k, threadIdx.x, kSplitNT);
+    if (sl == 0) write_identity(a.idx + (int64_t)t * a.k, n, a.k, threadIdx.x, kSplitNT);
     return;
   }
-
-  // first pass: the row histogram is complete (built by an earlier launch)
   const uint32_t* gh = a.hist + (int64_t)t * kBins1;
   for (int i = threadIdx.x; i < kBins1; i += kSplitNT) hist[i] = gh[i];
   __syncthreads();
   const BinSel s1 = select_bin<kSplitNT>(hist, kBins1, k, tmp, &res);
 
-  // this slice's candidates (keys in the boundary bin or above), in index order
   const int beg = sl * a.slice, end = min(n, beg + a.slice);
   uint2* mylist = a.lists + ((int64_t)t * a.nslices + sl) * a.slice;
   uint32_t mycnt = 0;
@@ -332,44 +342,68 @@ __global__ void __launch_bounds__(kSplitNT) topk_split_kernel(TopkArgs a) {
                               });
   }
   if (threadIdx.x == 0) a.slice_cnt[(int64_t)t * a.nslices + sl] = mycnt;
+}
 
-  // ticket: the last slice of the row to arrive finishes the selection
-  __threadfence();
-  __syncthreads();
-  if (threadIdx.x == 0) is_last = (atomicAdd(&a.counters[t], 1u) == (uint32_t)(a.nslices - 1)) ? 1u : 0u;
-  __syncthreads();
-  if (!is_last) return;
-  __threadfence();
+// Phase 2 of split mode (next launch, so every slice's list is visible): one
+// workgroup per row concatenates the slices' lists in slice order (= index
+// order), refines the boundary bin and emits the selection.
+__global__ void __launch_bounds__(kFinalNT) topk_finalize_kernel(TopkArgs a) {
+  __shared__ uint32_t hist[kBins1];
+  __shared__ uint32_t tmp[kFinalNT / 64];
+  __shared__ BinSel res;
+  __shared__ uint32_t lkey[kSplitCap];
+  __shared__ int lidx[kSplitCap];
+  __shared__ uint32_t cnt[kTopkMaxSlices];
+  __shared__ uint32_t offs[kTopkMaxSlices + 1];
 
+  const int t = blockIdx.x;
+  int b, pos;
+  row_seq_pos(a.g, t, b, pos);
+  const int n = pos + 1;
+  const uint32_t k = (uint32_t)a.k;
+  if (n <= a.k) return;                         // phase 1 wrote the identity selection
+  const uint32_t* gh = a.hist + (int64_t)t * kBins1;
+  for (int i = threadIdx.x; i < kBins1; i += kFinalNT) hist[i] = gh[i];
+  if (threadIdx.x < a.nslices) cnt[threadIdx.x] = a.slice_cnt[(int64_t)t * a.nslices + threadIdx.x];
+  __syncthreads();
   if (threadIdx.x == 0) {
     uint32_t o = 0;
     for (int s = 0; s < a.nslices; ++s) {
       offs[s] = o;
-      o += __atomic_load_n(&a.slice_cnt[(int64_t)t * a.nslices + s], __ATOMIC_RELAXED);
+      o += cnt[s];
     }
     offs[a.nslices] = o;
   }
-  __syncthreads();
+  const BinSel s1 = select_bin<kFinalNT>(hist, kBins1, k, tmp, &res);   // its barriers publish offs
   const uint32_t m = offs[a.nslices];
   const uint32_t need = k - s1.above;
+  int32_t* out = a.idx + (int64_t)t * a.k;
   auto to_out = [&](uint32_t slot, uint32_t, int id) { out[slot] = id; };
   const uint2* rowlists = a.lists + (int64_t)t * a.nslices * a.slice;
+  const SegSrc gs{rowlists, offs, a.nslices, a.slice};
   if (m <= (uint32_t)kSplitCap) {
-    for (int s = 0; s < a.nslices; ++s) {
-      const uint32_t c = offs[s + 1] - offs[s];
-      const uint2* src = rowlists + (int64_t)s * a.slice;
-      for (uint32_t i = threadIdx.x; i < c; i += kSplitNT) {
-        const uint2 e = src[i];
-        lkey[offs[s] + i] = e.x;
-        lidx[offs[s] + i] = (int)e.y;
-      }
+    for (int base = 0; base < (int)m; base += kFinalNT * 4 * kUnr) {
+      uint32_t key[kUnr][4];
+      int id[kUnr][4];
+      bool ok[kUnr][4];
+#pragma unroll
+      for (int u = 0; u < kUnr; ++u) gs.load4(base + (u * kFinalNT + threadIdx.x) * 4, key[u], id[u], ok[u]);
+#pragma unroll
+      for (int u = 0; u < kUnr; ++u)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int p = base + (u * kFinalNT + threadIdx.x) * 4 + j;
+          if (ok[u][j]) {
+            lkey[p] = key[u][j];
+            lidx[p] = id[u][j];
+          }
+        }
     }
     __syncthreads();
     const LdsSrc ls{lkey, lidx, (int)m};
-    refine_and_emit<kSplitNT>(ls, s1.bin, kBins1Bits, need, s1.cnt, hist, tmp, &res, k, to_out);
+    refine_and_emit<kFinalNT>(ls, s1.bin, kBins1Bits, need, s1.cnt, hist, tmp, &res, k, to_out);
   } else {
-    const SegSrc gs{rowlists, offs, a.nslices, a.slice};
-    refine_and_emit<kSplitNT>(gs, s1.bin, kBins1Bits, need, s1.cnt, hist, tmp, &res, k, to_out);
+    refine_and_emit<kFinalNT>(gs, s1.bin, kBins1Bits, need, s1.cnt, hist, tmp, &res, k, to_out);
   }
 }
 
@@ -392,7 +426,10 @@ hipError_t launch_topk_hist(const TopkArgs& a, hipStream_t stream) {
 }
 
 hipError_t launch_topk_split(const TopkArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL(topk_split_kernel, dim3(a.nslices, a.g.num_rows), dim3(kSplitNT), 0, stream, a);
+  hipLaunchKernelGGL(topk_slice_kernel, dim3(a.nslices, a.g.num_rows), dim3(kSplitNT), 0, stream, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(topk_finalize_kernel, dim3(a.g.num_rows), dim3(kFinalNT), 0, stream, a);
   return hipGetLastError();
 }
 

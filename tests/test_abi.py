@@ -71,6 +71,7 @@ def test_indexer_validation(lib):
     assert _indexer(lib, _batch(num_rows=3)) == _lib.DSA_ERR_SHAPE         # decode: rows must equal seqs
     assert _indexer(lib, _batch(seq_lens=None)) == _lib.DSA_ERR_NULL
     assert _indexer(lib, _batch(), H_I=65) == _lib.DSA_ERR_UNSUPPORTED
+    assert _indexer(lib, _batch(), H_I=6) == _lib.DSA_ERR_UNSUPPORTED
     assert _indexer(lib, _batch(), d_I=64) == _lib.DSA_ERR_UNSUPPORTED
     assert _indexer(lib, _batch(), q8=None) == _lib.DSA_ERR_NULL
     assert _indexer(lib, _batch(), scores=None) == _lib.DSA_ERR_NULL
