@@ -27,6 +27,12 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE,
           "-Wall", "-Wno-unused-function", "-Wno-unused-variable"]
 
 
+# Per-file extra flags.  The indexer keeps its MFMA accumulators in ordinary
+# VGPRs (its register budget allows it), so the epilogue reads them without
+# accumulator-register moves.
+FILE_FLAGS = {"indexer.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
 
@@ -37,7 +43,7 @@ def build(verbose: bool = False) -> str:
 
     def compile_one(src):
         obj = os.path.join(OBJDIR, os.path.basename(src) + ".o")
-        cmd = [HIPCC, *COMMON, *DEVICE_FLAGS, "-c", src, "-o", obj]
+        cmd = [HIPCC, *COMMON, *DEVICE_FLAGS, *FILE_FLAGS.get(os.path.basename(src), []), "-c", src, "-o", obj]
         r = subprocess.run(cmd, capture_output=True, text=True)
         out = "\n".join(l for l in (r.stdout + r.stderr).splitlines()
                         if "packed-fp32-ops' is not a recognized feature" not in l)

@@ -203,7 +203,9 @@ dsa_status run_indexer(const dsa_batch* b, const uint8_t* q8, const float* q_sca
   a.H_I = H_I;
   const bool decode = b->q_start == nullptr;
   if (decode) {
-    int64_t c = round_up(((int64_t)b->max_len * b->num_seqs + 1023) / 1024, 16);
+    // about 2048 workgroups over the batch: short enough chunks that the last
+    // wave of workgroups leaves little of the device idle
+    int64_t c = round_up(((int64_t)b->max_len * b->num_seqs + 2047) / 2048, 16);
     a.chunk = (int)(c < 256 ? 256 : (c > kIdxDecodeChunk ? kIdxDecodeChunk : c));
     a.ntiles = 1;
   } else {

@@ -256,7 +256,7 @@ __global__ void __launch_bounds__(256) indexer_kernel(IndexerArgs a) {
 // The DMA is inline asm and its completion is awaited with explicit
 // s_waitcnt vmcnt(N): DMA transfers are loads and complete in issue order, so
 // "at most (kRing-1)*PER memory ops outstanding" means the oldest tile landed.
-constexpr int kRing = 8;
+constexpr int kRing = 5;
 
 __device__ __forceinline__ int kswz(int n) { return (n >> 1) & 7; }
 
@@ -274,7 +274,8 @@ __global__ void __launch_bounds__(256) indexer_decode_ring_kernel(IndexerArgs a)
   __shared__ __attribute__((aligned(16))) char ring[4][kRing][SLOT];
 
   const int b = blockIdx.z;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
   const int nl = lane & 15, grp = lane >> 4;
 
   const int len = a.g.seq_lens[b];
@@ -284,38 +285,25 @@ __global__ void __launch_bounds__(256) indexer_decode_ring_kernel(IndexerArgs a)
   if constexpr (HIST) {
     for (int i = threadIdx.x; i < kBins1; i += 256) hist[i] = 0u;
   }
-
-  // query row b: widened A operands and folded head weights in registers
-  Wide<DI> qa[HT];
-  float wq[HT][4];
-  {
-    const float qs = a.q_scale ? a.q_scale[b] : 1.0f;
-#pragma unroll
-    for (int ht = 0; ht < HT; ++ht) {
-      const int h = ht * 16 + nl;
-      Frag<DI> raw;
-      if (h < a.H_I)
-        load_frag<DI, false>(raw, reinterpret_cast<const char*>(a.q8) + ((int64_t)b * a.H_I + h) * DI, grp);
-      else
-        zero_frag<DI>(raw);
-      qa[ht] = widen<DI>(raw);
-      // heads ht*16+4*grp .. +3 (H_I is a multiple of 4, rows 16-byte aligned)
-      const int hw = ht * 16 + grp * 4;
-      const float4 w4 = hw < a.H_I ? *reinterpret_cast<const float4*>(a.w + (int64_t)b * a.H_I + hw)
-                                   : make_float4(0.f, 0.f, 0.f, 0.f);
-      wq[ht][0] = w4.x * qs;
-      wq[ht][1] = w4.y * qs;
-      wq[ht][2] = w4.z * qs;
-      wq[ht][3] = w4.w * qs;
-    }
-  }
-  __builtin_amdgcn_s_waitcnt(0x0F70);         // operands are in; the ring owns vmcnt from here
-  if constexpr (HIST) __syncthreads();
+  // q_scale[b] through the scalar cache: a vector load here would make the
+  // compiler wait on the vector-memory counter, which the ring DMA shares
+  const float qs = a.q_scale ? *(const __attribute__((address_space(4))) float*)(uintptr_t)(a.q_scale + b) : 1.0f;
 
   const int ntiles = (kend - kbeg + 15) >> 4;
   const int my_tiles = ntiles > wave ? (ntiles - wave + 3) / 4 : 0;   // tiles wave, wave+4, ...
   char* myring = &ring[wave][0][0];
   const uint32_t ring_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)myring;
+
+  // Byte offsets, relative to the tile's first key row, of the two 16-byte
+  // chunks this lane moves for a full tile (slot chunk p = 64 i + lane holds
+  // chunk p & 7 ^ swizzle of key p >> 3), and of its key scale.  They do not
+  // change from tile to tile, so a full tile's DMA needs only a scalar base
+  // address.  32-bit offsets need 16 rows to span less than 2 GiB.
+  const bool off32 = a.kidx.row_stride < (1 << 26) && (!SCALE || a.ksc.row_stride < (1 << 26));
+  const int n0 = lane >> 3, n1 = 8 + (lane >> 3), pc = lane & 7;
+  const uint32_t koff0 = (uint32_t)(n0 * a.kidx.row_stride) + 16u * (uint32_t)(pc ^ kswz(n0));
+  const uint32_t koff1 = (uint32_t)(n1 * a.kidx.row_stride) + 16u * (uint32_t)(pc ^ kswz(n1));
+  const uint32_t soff = SCALE ? (uint32_t)(min(lane, 15) * a.ksc.row_stride) : 0u;
 
   // A 16-key tile never straddles a page (pages hold a power-of-two >= 16
   // tokens and tiles start at multiples of 16), so its keys are consecutive
@@ -338,30 +326,106 @@ __global__ void __launch_bounds__(256) indexer_decode_ring_kernel(IndexerArgs a)
     const int last = kend - 1 - s0;           // keys past the end re-read the last key
     const int64_t row0 = tile_row0(s0);
     const uint32_t slot = ring_lds + (uint32_t)((m % kRing) * SLOT);
+    if (last >= 15 && off32) {                // full tile: scalar base + fixed lane offsets
+      const char* kb = a.kidx.data + row0 * a.kidx.row_stride;
+      asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2 nt"
+                   :: "s"(slot), "v"(koff0), "s"(kb) : "memory");
+      asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2 nt"
+                   :: "s"(slot + 1024u), "v"(koff1), "s"(kb) : "memory");
+      if constexpr (SCALE) {
+        const char* sb = a.ksc.data + row0 * a.ksc.row_stride;
+        if (lane < 16)
+          asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, %2 nt"
+                       :: "s"(slot + 16u * DI), "v"(soff), "s"(sb) : "memory");
+      }
+    } else {                                  // ragged last tile: per-lane 64-bit addresses
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int p = i * 64 + lane;            // chunk position in the slot
-      const int n = p >> 3, pc = p & 7;
-      const char* src = a.kidx.data + (row0 + min(n, last)) * a.kidx.row_stride + 16 * (pc ^ kswz(n));
-      const uint32_t m0 = __builtin_amdgcn_readfirstlane(slot + i * 1024);
-      asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" :: "s"(m0), "v"(src) : "memory");
-    }
-    if constexpr (SCALE) {
-      const char* src = a.ksc.data + (row0 + min(lane, last)) * a.ksc.row_stride;
-      const uint32_t m0 = __builtin_amdgcn_readfirstlane(slot + 16 * DI);
-      if (lane < 16)
-        asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off" :: "s"(m0), "v"(src) : "memory");
+      for (int i = 0; i < 2; ++i) {
+        const int p = i * 64 + lane;
+        const int n = p >> 3;
+        const char* src = a.kidx.data + (row0 + min(n, last)) * a.kidx.row_stride + 16 * (pc ^ kswz(n));
+        asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off nt"
+                     :: "s"(slot + i * 1024u), "v"(src) : "memory");
+      }
+      if constexpr (SCALE) {
+        const char* src = a.ksc.data + (row0 + min(lane, last)) * a.ksc.row_stride;
+        if (lane < 16)
+          asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off nt"
+                       :: "s"(slot + 16u * DI), "v"(src) : "memory");
+      }
     }
   };
 
+  // The query row arrives through the ring as well: wave w moves indexer
+  // heads 16w..16w+15 (laid out and swizzled like a key tile) and their 16
+  // head weights into its last slot, then starts its first kRing-1 key tiles
+  // before anything waits, so the query and the first tiles are in flight
+  // together.  Heads past H_I re-read the last head and are zeroed on use.
+  {
+    const uint32_t slot = ring_lds + (uint32_t)((kRing - 1) * SLOT);
+    const char* qrow = reinterpret_cast<const char*>(a.q8) + (int64_t)b * a.H_I * DI;
+    const int qmax = a.H_I * DI - 16;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int p = i * 64 + lane;
+      const int n = p >> 3;
+      const char* src = qrow + min((wave * 16 + n) * DI + 16 * (pc ^ kswz(n)), qmax);
+      asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+                   :: "s"(slot + i * 1024u), "v"(src) : "memory");
+    }
+    const float* wsrc = a.w + (int64_t)b * a.H_I + min(wave * 16 + lane, a.H_I - 1);
+    if (lane < 16)
+      asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off"
+                   :: "s"(slot + 16u * DI), "v"(wsrc) : "memory");
+  }
   for (int m = 0; m < kRing - 1 && m < my_tiles; ++m) issue(m);
+  if (my_tiles >= kRing - 1)
+    wait_vmcnt<(kRing - 1) * PER>();          // this wave's query heads have landed
+  else
+    wait_vmcnt<0>();
+  // LDS-only fences: the barrier must not wait for the key tiles in flight
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 
   const int rb0 = nl * DI + 16 * ((2 * grp) ^ kswz(nl));
   const int rb1 = nl * DI + 16 * ((2 * grp + 1) ^ kswz(nl));
+
+  // widened A operands and folded head weights in registers
+  Wide<DI> qa[HT];
+  float wq[HT][4];
+#pragma unroll
+  for (int ht = 0; ht < HT; ++ht) {
+    const char* qslot = &ring[ht][kRing - 1][0];
+    Frag<DI> raw;
+    raw.lo = *reinterpret_cast<const v4i*>(qslot + rb0);
+    raw.hi = *reinterpret_cast<const v4i*>(qslot + rb1);
+    if (ht * 16 + nl >= a.H_I) zero_frag<DI>(raw);
+    qa[ht] = widen<DI>(raw);
+    // heads ht*16+4*grp .. +3 (H_I is a multiple of 4)
+    const float4 w4 = *reinterpret_cast<const float4*>(qslot + 16 * DI + 16 * grp);
+    const bool hv = ht * 16 + grp * 4 < a.H_I;
+    wq[ht][0] = hv ? w4.x * qs : 0.0f;
+    wq[ht][1] = hv ? w4.y * qs : 0.0f;
+    wq[ht][2] = hv ? w4.z * qs : 0.0f;
+    wq[ht][3] = hv ? w4.w * qs : 0.0f;
+  }
+  // every wave has read the query slots before any wave refills its last slot
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+
   for (int m = 0; m < my_tiles; ++m) {
     if (m + kRing - 1 < my_tiles) {
       issue(m + kRing - 1);
-      wait_vmcnt<(kRing - 1) * PER>();
+      // Global stores share the vector-memory counter with the DMA.  Every
+      // earlier iteration stored one score word (its tile was full: only the
+      // last tile of a chunk can be ragged, and that one waits for zero), so
+      // after the first kRing-1 tiles, kRing-1 stores sit behind tile m too.
+      if (m >= kRing - 1)
+        wait_vmcnt<(kRing - 1) * (PER + 1)>();
+      else
+        wait_vmcnt<(kRing - 1) * PER>();
     } else {
       wait_vmcnt<0>();
     }
@@ -375,13 +439,19 @@ __global__ void __launch_bounds__(256) indexer_decode_ring_kernel(IndexerArgs a)
 #pragma unroll
     for (int ht = 0; ht < HT; ++ht) {
       const v4f acc = mfma_dot<DI>(qa[ht], kb);
-      part = fmaf(wq[ht][0], fmaxf(acc[0], 0.0f), part);
-      part = fmaf(wq[ht][1], fmaxf(acc[1], 0.0f), part);
-      part = fmaf(wq[ht][2], fmaxf(acc[2], 0.0f), part);
-      part = fmaf(wq[ht][3], fmaxf(acc[3], 0.0f), part);
+      // ReLU as a clamp to [0, FLT_MAX]: the dot products are finite
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        part = fmaf(wq[ht][i], __builtin_amdgcn_fmed3f(acc[i], 0.0f, 3.402823466e38f), part);
     }
-    part += __shfl_xor(part, 16);
-    part += __shfl_xor(part, 32);
+    // sum over the four lane groups (rows of 16 lanes) holding key nl:
+    // the row swaps give every lane its neighbours' partial sums
+    {
+      const auto r16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(part), __float_as_uint(part), false, false);
+      part = __uint_as_float(r16[0]) + __uint_as_float(r16[1]);
+      const auto r32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(part), __float_as_uint(part), false, false);
+      part = __uint_as_float(r32[0]) + __uint_as_float(r32[1]);
+    }
     const int s = kbeg + ((wave + 4 * m) << 4) + nl;
     if (grp == 0 && s < kend) {
       const float sc = part * ks;
