@@ -28,6 +28,38 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, vendor figure
 
+# HBM traffic of one decode-indexer launch on this workload, from rocprofv3
+# counters (FETCH_SIZE and WRITE_SIZE in KiB per dispatch, averaged over the
+# launches of a short bench run), scaled by what the same counters read for a
+# 1 GiB device copy: fetch x2.0, write x1.0.  The figures hold only for the
+# kernel sources they were taken on; any change to them reports null.
+INDEXER_COUNTERS = {
+    "sources": ["sparse_attention_long_06_amd/csrc/indexer.hip", "sparse_attention_long_06_amd/csrc/dsa_common.h",
+                "sparse_attention_long_06_amd/csrc/dsa_kernels.h", "sparse_attention_long_06_amd/csrc/api.hip"],
+    "sha256": None,
+    "fetch_kib": None,
+    "write_kib": None,
+    "fetch_scale": 2.0,
+    "write_scale": 1.0,
+}
+
+
+def indexer_sources_sha256() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for rel in INDEXER_COUNTERS["sources"]:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def indexer_traffic_bytes():
+    """Counter-measured HBM bytes per indexer launch, or None if the sources changed since."""
+    c = INDEXER_COUNTERS
+    if c["sha256"] is None or c["sha256"] != indexer_sources_sha256():
+        return None
+    return int(round(c["fetch_kib"] * 1024 * c["fetch_scale"] + c["write_kib"] * 1024 * c["write_scale"]))
+
 
 def _hip():
     lib = ctypes.CDLL("libamdhip64.so")
@@ -145,9 +177,9 @@ def run_bench(args):
                    "parallelism": "single GPU"},
         "tokens_per_s": round(qps, 1),
         "context_tokens_scanned_per_s": round(ctx_total / (elapsed / args.steps), 1),
-        "roofline": {"bound": "hbm", "kernel": "indexer_kernel (decode layout, fused top-k histogram)",
+        "roofline": {"bound": "hbm", "kernel": "indexer_decode_ring_kernel (decode indexer + first top-k histogram)",
                      "achieved": round(idx_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(idx_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(idx_gbs / HBM_PEAK_GBS, 4), "traffic": indexer_traffic_bytes(),
                      "bytes_per_launch": idx_bytes, "launch_ms": round(stage_ms["indexer"], 4)},
         "stages_ms": {k: round(v, 4) for k, v in stage_ms.items()},
         "step_hbm": {"bytes": idx_bytes + other_bytes, "GB/s": round(step_gbs, 1),
@@ -175,15 +207,15 @@ def cpu_baseline(inp, budget_s: float):
         threads = os.cpu_count()
     done = 0
     t0 = time.perf_counter()
-    for r in range(B):
-        oracle.run_rows(a, [r])
+    while True:                       # cycle over the batch's queries until the budget is spent
+        oracle.run_rows(a, [done % B])
         done += 1
         if time.perf_counter() - t0 >= budget_s:
             break
     el = time.perf_counter() - t0
     return {"value": round(done / el, 4), "unit": "queries/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{done} of {B} decode queries of {wl.name} (each: indexer over {wl.seq_len} tokens, "
-                      f"top-{wl.k}, attention), fp64 NumPy, {el:.1f} s"}
+            "sample": f"{done} decode queries cycling over the {B} of {wl.name} (each: indexer over "
+                      f"{wl.seq_len} tokens, top-{wl.k}, attention), fp64 NumPy, {el:.1f} s"}
 
 
 def copy_calibration(nbytes: int):

@@ -38,6 +38,12 @@ typedef __attribute__((address_space(3))) v4s lds_v4s;
 
 __device__ __forceinline__ int swz(int r) { return (r >> 1) & 7; }
 
+// Workgroup id renumbered so that ids dealt to the same XCD (id % 8) form a
+// contiguous range; identity when the grid is not a multiple of 8.
+__device__ __forceinline__ int xcd_major(int id, int n) {
+  return (n & 7) ? id : (id & 7) * (n >> 3) + (id >> 3);
+}
+
 // s_waitcnt immediate for "vmcnt(0)" on gfx9-family parts: vmcnt bits [3:0]
 // and [15:14] zero, expcnt [6:4] and lgkmcnt [11:8] at their maximum.
 constexpr int kWaitVmcnt0 = 0x0F70;
@@ -86,8 +92,13 @@ __global__ void __launch_bounds__(512) attn_kernel(AttnArgs a) {
   __shared__ uint8_t valid[MAXROWS];
 
   const int waves = blockDim.x >> 6;
-  const int split = blockIdx.x % a.nsplit;
-  const int t = blockIdx.x / a.nsplit;
+  // Workgroups are dealt to the 8 XCDs round-robin by id.  Renumber them so
+  // that each XCD gets a contiguous run of (row, split) items: the splits of
+  // a row then share one L2, which serves their common q after the first read
+  // and keeps the partials near the combine that reads them.
+  const int wg = xcd_major(blockIdx.x, gridDim.x);
+  const int split = wg % a.nsplit;
+  const int t = wg / a.nsplit;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int nl = lane & 15, grp = lane >> 4;
   const int h0 = wave * 16 * HW;
@@ -312,7 +323,8 @@ __global__ void __launch_bounds__(512) attn_kernel(AttnArgs a) {
 // One thread per 8 consecutive value dims of one head.
 __global__ void __launch_bounds__(256) attn_combine_kernel(CombineArgs a) {
   const int per_head = a.D_v / 8;
-  const int64_t item = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  // same XCD-major order as the attention workgroups that wrote the partials
+  const int64_t item = (int64_t)xcd_major(blockIdx.x, gridDim.x) * blockDim.x + threadIdx.x;
   const int64_t total = (int64_t)a.T * a.H * per_head;
   if (item >= total) return;
   const int d8 = (int)(item % per_head);

@@ -81,15 +81,25 @@ __device__ __forceinline__ float wave_max(float x) {
 // Exclusive scan of one uint32 per thread over a block of NT threads.
 // `tmp` holds NT/64 words of LDS.  Returns the exclusive prefix; `total`
 // receives the block total.  Contains two barriers.
+// Inclusive prefix sum over the 64 lanes of a wave with DPP moves only (no
+// LDS traffic): Hillis-Steele inside each 16-lane row by row shifts, then the
+// row totals carried across rows by the row_bcast:15 / row_bcast:31 forms.
+// A lane whose DPP source falls outside its row, or whose row is masked off,
+// adds the `old` operand, 0.
+__device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t x) {
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xf, 0xf, false);  // row_shr:1
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xf, 0xf, false);  // row_shr:2
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xf, 0xf, false);  // row_shr:4
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xf, 0xf, false);  // row_shr:8
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x142, 0xa, 0xf, false);  // row_bcast:15 -> rows 1, 3
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x143, 0xc, 0xf, false);  // row_bcast:31 -> rows 2, 3
+  return x;
+}
+
 template <int NT>
 __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* tmp, uint32_t& total) {
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-  uint32_t x = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const uint32_t y = __shfl_up(x, o);
-    if (lane >= o) x += y;
-  }
+  const uint32_t x = wave_inclusive_scan(v);
   if (lane == 63) tmp[wid] = x;
   __syncthreads();
   uint32_t before = 0, tot = 0;

@@ -41,18 +41,25 @@ struct BinSel {
 
 // ---- element sources: size() and load4(i, ...) for i a multiple of 4
 
+// load4_full(i, ...) may assume i + 3 < size(): callers use it for chunks
+// that lie wholly inside the source, where it compiles to one branch-free
+// vector load, so a batch of them is issued before the first result is
+// awaited.  load4 handles the ragged end.
 struct RowSrc {  // fp32 scores in global memory; token index = base + i
-  const float* p;
+  const float* p;  // 16-byte aligned (score rows are, and slices start at multiples of 4)
   int n;
   int base;
   __device__ int size() const { return n; }
-  __device__ void load4(int i, uint32_t (&key)[4], int (&id)[4], bool (&ok)[4]) const {
-    if (i + 3 < n && ((reinterpret_cast<uintptr_t>(p + i) & 15) == 0)) {
-      const float4 v = *reinterpret_cast<const float4*>(p + i);
-      key[0] = score_key(v.x); key[1] = score_key(v.y);
-      key[2] = score_key(v.z); key[3] = score_key(v.w);
+  __device__ __forceinline__ void load4_full(int i, uint32_t (&key)[4], int (&id)[4], bool (&ok)[4]) const {
+    const float4 v = *reinterpret_cast<const float4*>(p + i);
+    key[0] = score_key(v.x); key[1] = score_key(v.y);
+    key[2] = score_key(v.z); key[3] = score_key(v.w);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) { id[j] = base + i + j; ok[j] = true; }
+    for (int j = 0; j < 4; ++j) { id[j] = base + i + j; ok[j] = true; }
+  }
+  __device__ __forceinline__ void load4(int i, uint32_t (&key)[4], int (&id)[4], bool (&ok)[4]) const {
+    if (i + 3 < n) {
+      load4_full(i, key, id, ok);
     } else {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -69,7 +76,7 @@ struct LdsSrc {  // (key, index) pairs in LDS
   const int* id;
   int n;
   __device__ int size() const { return n; }
-  __device__ void load4(int i, uint32_t (&k)[4], int (&d)[4], bool (&ok)[4]) const {
+  __device__ __forceinline__ void load4(int i, uint32_t (&k)[4], int (&d)[4], bool (&ok)[4]) const {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       ok[j] = i + j < n;
@@ -77,6 +84,7 @@ struct LdsSrc {  // (key, index) pairs in LDS
       d[j] = ok[j] ? id[i + j] : -1;
     }
   }
+  __device__ __forceinline__ void load4_full(int i, uint32_t (&k)[4], int (&d)[4], bool (&ok)[4]) const { load4(i, k, d, ok); }
 };
 
 struct SegSrc {  // per-slice (key, index) lists in global memory, concatenated in slice order
@@ -85,7 +93,7 @@ struct SegSrc {  // per-slice (key, index) lists in global memory, concatenated 
   int nslices;
   int slice;
   __device__ int size() const { return (int)offs[nslices]; }
-  __device__ void load4(int i, uint32_t (&k)[4], int (&d)[4], bool (&ok)[4]) const {
+  __device__ __forceinline__ void load4(int i, uint32_t (&k)[4], int (&d)[4], bool (&ok)[4]) const {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const uint32_t pos = (uint32_t)(i + j);
@@ -104,6 +112,7 @@ struct SegSrc {  // per-slice (key, index) lists in global memory, concatenated 
       }
     }
   }
+  __device__ __forceinline__ void load4_full(int i, uint32_t (&k)[4], int (&d)[4], bool (&ok)[4]) const { load4(i, k, d, ok); }
 };
 
 // ---- block-level building blocks (every thread of the block calls them)
@@ -112,9 +121,36 @@ struct SegSrc {  // per-slice (key, index) lists in global memory, concatenated 
 // them is consumed: global sources are latency-bound otherwise.
 constexpr int kUnr = 8;
 
+// kUnr chunks of 4 elements per thread starting at `base`; whole chunks go
+// through load4_full (issued back to back), a ragged batch through load4.
+template <int NT, class Src>
+__device__ __forceinline__ void load_batch(const Src& src, int base, uint32_t (&key)[kUnr][4], int (&id)[kUnr][4],
+                                           bool (&ok)[kUnr][4]) {
+  if (base + NT * 4 * kUnr <= src.size()) {       // uniform
+#pragma unroll
+    for (int u = 0; u < kUnr; ++u) src.load4_full(base + (u * NT + threadIdx.x) * 4, key[u], id[u], ok[u]);
+  } else {
+#pragma unroll
+    for (int u = 0; u < kUnr; ++u) src.load4(base + (u * NT + threadIdx.x) * 4, key[u], id[u], ok[u]);
+  }
+}
+
+// Copy a kBins1-bin row histogram from global memory to LDS; every thread
+// issues all of its (16-byte) loads before storing any.
+template <int NT>
+__device__ __forceinline__ void load_hist(const uint32_t* gh, uint32_t* hist) {
+  constexpr int PER = kBins1 / (4 * NT);
+  static_assert(PER >= 1 && kBins1 % (4 * NT) == 0, "histogram copy shape");
+  uint4 v[PER];
+#pragma unroll
+  for (int j = 0; j < PER; ++j) v[j] = reinterpret_cast<const uint4*>(gh)[j * NT + threadIdx.x];
+#pragma unroll
+  for (int j = 0; j < PER; ++j) reinterpret_cast<uint4*>(hist)[j * NT + threadIdx.x] = v[j];
+}
+
 // Histogram of bits [shift, shift+bits) of the keys whose top `pbits` bits equal P.
 template <int NT, class Src>
-__device__ void hist_pass(const Src& src, uint32_t* hist, uint32_t P, int pbits, int shift, int bits) {
+__device__ __forceinline__ void hist_pass(const Src& src, uint32_t* hist, uint32_t P, int pbits, int shift, int bits) {
   const int nb = 1 << bits;
   for (int i = threadIdx.x; i < nb; i += NT) hist[i] = 0u;
   __syncthreads();
@@ -124,8 +160,7 @@ __device__ void hist_pass(const Src& src, uint32_t* hist, uint32_t P, int pbits,
     uint32_t key[kUnr][4];
     int id[kUnr][4];
     bool ok[kUnr][4];
-#pragma unroll
-    for (int u = 0; u < kUnr; ++u) src.load4(base + (u * NT + threadIdx.x) * 4, key[u], id[u], ok[u]);
+    load_batch<NT>(src, base, key, id, ok);
 #pragma unroll
     for (int u = 0; u < kUnr; ++u)
 #pragma unroll
@@ -139,7 +174,7 @@ __device__ void hist_pass(const Src& src, uint32_t* hist, uint32_t P, int pbits,
 // The bin (scanning from the top) where the running count reaches `need`,
 // how many keys lie in higher bins, and how many are in the bin.
 template <int NT>
-__device__ BinSel select_bin(const uint32_t* hist, int nb, uint32_t need, uint32_t* tmp, BinSel* res) {
+__device__ __forceinline__ BinSel select_bin(const uint32_t* hist, int nb, uint32_t need, uint32_t* tmp, BinSel* res) {
   const int per = (nb + NT - 1) / NT;
   uint32_t c = 0;
   for (int j = 0; j < per; ++j) {
@@ -173,46 +208,56 @@ __device__ BinSel select_bin(const uint32_t* hist, int nb, uint32_t need, uint32
 // top-`pbits` key prefix is greater than P plus the first `need_eq` whose
 // prefix equals P; emit(slot, key, index) gets consecutive slots.  Stops once
 // `target` elements are out.  Returns the number emitted (uniform).
+//
+// compact_chunk handles one chunk of NT*4 elements (4 per thread, already
+// loaded); gt_base/eq_base carry the counts of the chunks before it.
+template <int NT, class Emit>
+__device__ __forceinline__ void compact_chunk(const uint32_t (&key)[4], const int (&id)[4], const bool (&ok)[4],
+                                              uint32_t P, int shift, uint32_t need_eq, uint32_t* tmp,
+                                              uint32_t& gt_base, uint32_t& eq_base, Emit& emit) {
+  uint32_t fgt = 0, feq = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    if (ok[j]) {
+      const uint32_t pre = key[j] >> shift;
+      if (pre > P) fgt |= 1u << j;
+      else if (pre == P) feq |= 1u << j;
+    }
+  }
+  const uint32_t packed = (uint32_t)__popc(fgt) | ((uint32_t)__popc(feq) << 16);
+  uint32_t tot;
+  const uint32_t ex = block_exclusive_scan<NT>(packed, tmp, tot);
+  uint32_t gt = gt_base + (ex & 0xFFFFu), eq = eq_base + (ex >> 16);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    if ((fgt >> j) & 1u) {
+      emit(gt + min(eq, need_eq), key[j], id[j]);
+      ++gt;
+    } else if ((feq >> j) & 1u) {
+      if (eq < need_eq) emit(gt + eq, key[j], id[j]);
+      ++eq;
+    }
+  }
+  gt_base += tot & 0xFFFFu;
+  eq_base += tot >> 16;
+}
+
 template <int NT, class Src, class Emit>
-__device__ uint32_t compact(const Src& src, uint32_t P, int pbits, uint32_t need_eq, uint32_t target,
-                           uint32_t* tmp, Emit emit) {
+__device__ __forceinline__ uint32_t compact(const Src& src, uint32_t P, int pbits, uint32_t need_eq, uint32_t target,
+                           uint32_t* tmp, Emit emit, int start = 0, uint32_t gt0 = 0, uint32_t eq0 = 0) {
   const int shift = 32 - pbits;
-  uint32_t gt_base = 0, eq_base = 0;
+  uint32_t gt_base = gt0, eq_base = eq0;
+  if (gt_base + min(eq_base, need_eq) >= target) return gt_base + min(eq_base, need_eq);
   const int n = src.size();
-  for (int base = 0; base < n; base += NT * 4 * kUnr) {
+  for (int base = start; base < n; base += NT * 4 * kUnr) {
     uint32_t key[kUnr][4];
     int id[kUnr][4];
     bool ok[kUnr][4];
-#pragma unroll
-    for (int u = 0; u < kUnr; ++u) src.load4(base + (u * NT + threadIdx.x) * 4, key[u], id[u], ok[u]);
+    load_batch<NT>(src, base, key, id, ok);
 #pragma unroll
     for (int u = 0; u < kUnr; ++u) {
       if (base + u * NT * 4 >= n) break;              // uniform
-      uint32_t fgt = 0, feq = 0;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        if (ok[u][j]) {
-          const uint32_t pre = key[u][j] >> shift;
-          if (pre > P) fgt |= 1u << j;
-          else if (pre == P) feq |= 1u << j;
-        }
-      }
-      const uint32_t packed = (uint32_t)__popc(fgt) | ((uint32_t)__popc(feq) << 16);
-      uint32_t tot;
-      const uint32_t ex = block_exclusive_scan<NT>(packed, tmp, tot);
-      uint32_t gt = gt_base + (ex & 0xFFFFu), eq = eq_base + (ex >> 16);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        if ((fgt >> j) & 1u) {
-          emit(gt + min(eq, need_eq), key[u][j], id[u][j]);
-          ++gt;
-        } else if ((feq >> j) & 1u) {
-          if (eq < need_eq) emit(gt + eq, key[u][j], id[u][j]);
-          ++eq;
-        }
-      }
-      gt_base += tot & 0xFFFFu;
-      eq_base += tot >> 16;
+      compact_chunk<NT>(key[u], id[u], ok[u], P, shift, need_eq, tmp, gt_base, eq_base, emit);
       if (gt_base + min(eq_base, need_eq) >= target) return gt_base + min(eq_base, need_eq);
     }
   }
@@ -222,7 +267,7 @@ __device__ uint32_t compact(const Src& src, uint32_t P, int pbits, uint32_t need
 // Refine (P, pbits) until the boundary bin is needed whole or the key is
 // exhausted, then emit the selection in source order.
 template <int NT, class Src, class Emit>
-__device__ void refine_and_emit(const Src& src, uint32_t P, int pbits, uint32_t need, uint32_t cnt,
+__device__ __forceinline__ void refine_and_emit(const Src& src, uint32_t P, int pbits, uint32_t need, uint32_t cnt,
                                 uint32_t* hist, uint32_t* tmp, BinSel* res, uint32_t target, Emit emit) {
   while (cnt != need && pbits < 32) {
     const int bits = (pbits + 11 <= 22) ? 11 : 32 - pbits;
@@ -326,21 +371,49 @@ __global__ void __launch_bounds__(kSplitNT) topk_slice_kernel(TopkArgs a) {
     if (sl == 0) write_identity(a.idx + (int64_t)t * a.k, n, a.k, threadIdx.x, kSplitNT);
     return;
   }
-  const uint32_t* gh = a.hist + (int64_t)t * kBins1;
-  for (int i = threadIdx.x; i < kBins1; i += kSplitNT) hist[i] = gh[i];
+  // The slice's first NT*4*kUnr scores are requested before the row
+  // histogram, so the two memory latencies overlap instead of adding up.
+  const int beg = sl * a.slice, end = min(n, beg + a.slice);
+  const RowSrc src{a.scores + (int64_t)t * a.ld + beg, max(end - beg, 0), beg};
+  constexpr int kFirst = kSplitNT * 4 * kUnr;
+  uint32_t key[kUnr][4];
+  int id[kUnr][4];
+  bool ok[kUnr][4];
+  const bool full = src.size() >= kFirst;     // uniform
+  float4 raw[kUnr];
+  if (full) {
+#pragma unroll
+    for (int u = 0; u < kUnr; ++u) raw[u] = *reinterpret_cast<const float4*>(src.p + (u * kSplitNT + threadIdx.x) * 4);
+  }
+
+  load_hist<kSplitNT>(a.hist + (int64_t)t * kBins1, hist);
   __syncthreads();
   const BinSel s1 = select_bin<kSplitNT>(hist, kBins1, k, tmp, &res);
 
-  const int beg = sl * a.slice, end = min(n, beg + a.slice);
-  uint2* mylist = a.lists + ((int64_t)t * a.nslices + sl) * a.slice;
-  uint32_t mycnt = 0;
-  if (beg < end) {
-    const RowSrc src{a.scores + (int64_t)t * a.ld + beg, end - beg, beg};
-    mycnt = compact<kSplitNT>(src, s1.bin, kBins1Bits, 0xFFFFFFFFu, 0xFFFFFFFFu, tmp,
-                              [&](uint32_t slot, uint32_t key, int id) {
-                                mylist[slot] = make_uint2(key, (uint32_t)id);
-                              });
+  if (full) {
+#pragma unroll
+    for (int u = 0; u < kUnr; ++u) {
+      const int i = (u * kSplitNT + threadIdx.x) * 4;
+      key[u][0] = score_key(raw[u].x); key[u][1] = score_key(raw[u].y);
+      key[u][2] = score_key(raw[u].z); key[u][3] = score_key(raw[u].w);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) { id[u][j] = beg + i + j; ok[u][j] = true; }
+    }
+  } else {
+    load_batch<kSplitNT>(src, 0, key, id, ok);
   }
+
+  uint2* mylist = a.lists + ((int64_t)t * a.nslices + sl) * a.slice;
+  auto to_list = [&](uint32_t slot, uint32_t kk, int ii) { mylist[slot] = make_uint2(kk, (uint32_t)ii); };
+  uint32_t gt = 0, eq = 0;
+#pragma unroll
+  for (int u = 0; u < kUnr; ++u) {
+    if (u * kSplitNT * 4 >= src.size()) break;       // uniform
+    compact_chunk<kSplitNT>(key[u], id[u], ok[u], s1.bin, 32 - kBins1Bits, 0xFFFFFFFFu, tmp, gt, eq, to_list);
+  }
+  const uint32_t mycnt = src.size() > kFirst
+      ? compact<kSplitNT>(src, s1.bin, kBins1Bits, 0xFFFFFFFFu, 0xFFFFFFFFu, tmp, to_list, kFirst, gt, eq)
+      : gt + eq;
   if (threadIdx.x == 0) a.slice_cnt[(int64_t)t * a.nslices + sl] = mycnt;
 }
 
@@ -362,8 +435,7 @@ __global__ void __launch_bounds__(kFinalNT) topk_finalize_kernel(TopkArgs a) {
   const int n = pos + 1;
   const uint32_t k = (uint32_t)a.k;
   if (n <= a.k) return;                         // phase 1 wrote the identity selection
-  const uint32_t* gh = a.hist + (int64_t)t * kBins1;
-  for (int i = threadIdx.x; i < kBins1; i += kFinalNT) hist[i] = gh[i];
+  load_hist<kFinalNT>(a.hist + (int64_t)t * kBins1, hist);
   if (threadIdx.x < a.nslices) cnt[threadIdx.x] = a.slice_cnt[(int64_t)t * a.nslices + threadIdx.x];
   __syncthreads();
   if (threadIdx.x == 0) {
