@@ -107,8 +107,8 @@ Cache make_cache(const dsa_cache* c) {
 struct TopkPlan {
   bool split = false;
   int nslices = 0, slice = 0;
-  size_t off_hist = 0, off_slice = 0, off_lists = 0, bytes = 0;
-  size_t zero_words = 0;  // the histograms, from off_hist
+  size_t off_hist = 0, off_hist2 = 0, off_meta = 0, off_slice = 0, off_lists = 0, bytes = 0;
+  size_t zero_words = 0;  // the two histograms, from off_hist
 };
 
 TopkPlan plan_topk(int T, int max_len, int k) {
@@ -127,7 +127,9 @@ TopkPlan plan_topk(int T, int max_len, int k) {
   p.nslices = ns;
   size_t o = 0;
   p.off_hist = o; o += (size_t)T * kBins1 * 4;
+  p.off_hist2 = o; o += (size_t)T * kBins1 * 4;
   p.zero_words = o / 4;
+  p.off_meta = o; o += (size_t)T * 16;
   p.off_slice = o; o += (size_t)T * ns * 4;
   o = (size_t)round_up((int64_t)o, 256);
   p.off_lists = o; o += (size_t)T * ns * slice * 8;
@@ -227,6 +229,8 @@ dsa_status run_topk(const dsa_batch* b, const float* scores, int64_t ld, int k, 
   a.k = k;
   a.idx = idx;
   a.hist = nullptr;
+  a.hist2 = nullptr;
+  a.meta = nullptr;
   a.slice_cnt = nullptr;
   a.lists = nullptr;
   a.slice = p.slice;
@@ -236,6 +240,8 @@ dsa_status run_topk(const dsa_batch* b, const float* scores, int64_t ld, int k, 
     return DSA_OK;
   }
   a.hist = reinterpret_cast<uint32_t*>(ws + p.off_hist);
+  a.hist2 = reinterpret_cast<uint32_t*>(ws + p.off_hist2);
+  a.meta = reinterpret_cast<uint32_t*>(ws + p.off_meta);
   a.slice_cnt = reinterpret_cast<uint32_t*>(ws + p.off_slice);
   a.lists = reinterpret_cast<uint2*>(ws + p.off_lists);
   if (!hist_ready) {

@@ -81,6 +81,15 @@ __device__ __forceinline__ float wave_max(float x) {
 // Exclusive scan of one uint32 per thread over a block of NT threads.
 // `tmp` holds NT/64 words of LDS.  Returns the exclusive prefix; `total`
 // receives the block total.  Contains two barriers.
+// Workgroup barrier that orders LDS only.  __syncthreads() also makes every
+// wave wait for its outstanding global stores and atomics; where the barrier
+// only publishes LDS data, that wait is pure latency.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // Inclusive prefix sum over the 64 lanes of a wave with DPP moves only (no
 // LDS traffic): Hillis-Steele inside each 16-lane row by row shifts, then the
 // row totals carried across rows by the row_bcast:15 / row_bcast:31 forms.
@@ -101,7 +110,7 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* t
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const uint32_t x = wave_inclusive_scan(v);
   if (lane == 63) tmp[wid] = x;
-  __syncthreads();
+  lds_barrier();
   uint32_t before = 0, tot = 0;
 #pragma unroll
   for (int w = 0; w < NT / 64; ++w) {
@@ -109,7 +118,7 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* t
     before += (w < wid) ? s : 0u;
     tot += s;
   }
-  __syncthreads();
+  lds_barrier();
   total = tot;
   return before + x - v;
 }

@@ -41,7 +41,9 @@ struct TopkArgs {
   int64_t ld;
   int k;
   int32_t* idx;          // [T, k]
-  uint32_t* hist;        // [T, kBins1]           (split mode)
+  uint32_t* hist;        // [T, kBins1]           (split mode) first-pass row histogram
+  uint32_t* hist2;       // [T, kBins1]           (split mode) next 11 bits of the boundary bin
+  uint32_t* meta;        // [T, 4]                (split mode) first-pass bin, count above it, count in it
   uint32_t* slice_cnt;   // [T, nslices]          (split mode)
   uint2* lists;          // [T, nslices * slice]  (split mode)
   int slice;             // keys per slice        (split mode)

@@ -467,7 +467,7 @@ __global__ void __launch_bounds__(256) indexer_decode_ring_kernel(IndexerArgs a)
   }
 
   if constexpr (HIST) {
-    __syncthreads();
+    lds_barrier();                            // the histogram is complete; score stores may still be in flight
     uint32_t* gh = a.hist + (int64_t)b * kBins1;
     for (int i = threadIdx.x; i < kBins1; i += 256) {
       const uint32_t c = hist[i];

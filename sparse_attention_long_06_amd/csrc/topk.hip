@@ -153,7 +153,7 @@ template <int NT, class Src>
 __device__ __forceinline__ void hist_pass(const Src& src, uint32_t* hist, uint32_t P, int pbits, int shift, int bits) {
   const int nb = 1 << bits;
   for (int i = threadIdx.x; i < nb; i += NT) hist[i] = 0u;
-  __syncthreads();
+  lds_barrier();
   const uint32_t mask = (uint32_t)nb - 1u;
   const int n = src.size();
   for (int base = 0; base < n; base += NT * 4 * kUnr) {
@@ -168,7 +168,7 @@ __device__ __forceinline__ void hist_pass(const Src& src, uint32_t* hist, uint32
         if (ok[u][j] && (pbits == 0 || (key[u][j] >> (32 - pbits)) == P))
           atomicAdd(&hist[(key[u][j] >> shift) & mask], 1u);
   }
-  __syncthreads();
+  lds_barrier();
 }
 
 // The bin (scanning from the top) where the running count reaches `need`,
@@ -198,68 +198,100 @@ __device__ __forceinline__ BinSel select_bin(const uint32_t* hist, int nb, uint3
       run += h;
     }
   }
-  __syncthreads();
+  lds_barrier();
   const BinSel r = *res;
-  __syncthreads();
+  lds_barrier();
   return r;
 }
 
 // Ordered compaction: in ascending source order, emit every element whose
 // top-`pbits` key prefix is greater than P plus the first `need_eq` whose
-// prefix equals P; emit(slot, key, index) gets consecutive slots.  Stops once
-// `target` elements are out.  Returns the number emitted (uniform).
+// prefix equals P; emit(slot, key, index) gets consecutive slots.
 //
-// compact_chunk handles one chunk of NT*4 elements (4 per thread, already
-// loaded); gt_base/eq_base carry the counts of the chunks before it.
+// compact_batch does one batch already in registers (kUnr chunks of 4
+// elements per thread, chunk u covering elements (u*NT + thread)*4 + j).  The
+// kUnr packed (greater, equal) chunk counts are scanned together, one barrier
+// pair per batch, and each thread then walks only its set bits, so the cost
+// follows the few elements kept.  gt_base / eq_base (uniform) count the
+// elements of earlier batches and are advanced past this one.  tmp holds
+// kUnr * NT/64 words.
 template <int NT, class Emit>
-__device__ __forceinline__ void compact_chunk(const uint32_t (&key)[4], const int (&id)[4], const bool (&ok)[4],
-                                              uint32_t P, int shift, uint32_t need_eq, uint32_t* tmp,
-                                              uint32_t& gt_base, uint32_t& eq_base, Emit& emit) {
-  uint32_t fgt = 0, feq = 0;
+__device__ __forceinline__ void compact_batch(const uint32_t (&key)[kUnr][4], const int (&id)[kUnr][4],
+                                              const bool (&ok)[kUnr][4], uint32_t P, int shift, uint32_t need_eq,
+                                              uint32_t* tmp, uint32_t& gt_base, uint32_t& eq_base, Emit& emit) {
+  constexpr int NW = NT / 64;
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  uint32_t mg[kUnr], me[kUnr], inc[kUnr], own[kUnr];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    if (ok[j]) {
-      const uint32_t pre = key[j] >> shift;
-      if (pre > P) fgt |= 1u << j;
-      else if (pre == P) feq |= 1u << j;
+  for (int u = 0; u < kUnr; ++u) {
+    mg[u] = 0u;
+    me[u] = 0u;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {        // branch-free: selects, no exec-mask juggling
+      const uint32_t pre = key[u][j] >> shift;
+      const uint32_t v = ok[u][j] ? 1u : 0u;
+      mg[u] |= (v & (pre > P ? 1u : 0u)) << j;
+      me[u] |= (v & (pre == P ? 1u : 0u)) << j;
+    }
+    own[u] = (uint32_t)__popc(mg[u]) | ((uint32_t)__popc(me[u]) << 16);
+    inc[u] = wave_inclusive_scan(own[u]);
+    if (lane == 63) tmp[u * NW + wid] = inc[u];
+  }
+  lds_barrier();
+  uint32_t gt0[kUnr], eq0[kUnr];
+  uint32_t rg = gt_base, re = eq_base;
+#pragma unroll
+  for (int u = 0; u < kUnr; ++u) {
+    uint32_t before = 0, tot = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const uint32_t c = tmp[u * NW + w];
+      before += (w < wid) ? c : 0u;
+      tot += c;
+    }
+    const uint32_t ex = before + inc[u] - own[u];
+    gt0[u] = rg + (ex & 0xFFFFu);
+    eq0[u] = re + (ex >> 16);
+    rg += tot & 0xFFFFu;
+    re += tot >> 16;
+  }
+  lds_barrier();
+  gt_base = rg;
+  eq_base = re;
+#pragma unroll
+  for (int u = 0; u < kUnr; ++u) {
+    uint32_t mm = mg[u] | me[u], gt = gt0[u], eq = eq0[u];
+    while (mm) {
+      const int j = __builtin_ctz(mm);
+      const uint32_t kk = j == 0 ? key[u][0] : j == 1 ? key[u][1] : j == 2 ? key[u][2] : key[u][3];
+      const int ii = j == 0 ? id[u][0] : j == 1 ? id[u][1] : j == 2 ? id[u][2] : id[u][3];
+      if ((mg[u] >> j) & 1u) {
+        emit(gt + min(eq, need_eq), kk, ii);
+        ++gt;
+      } else {
+        if (eq < need_eq) emit(gt + eq, kk, ii);
+        ++eq;
+      }
+      mm &= mm - 1u;
     }
   }
-  const uint32_t packed = (uint32_t)__popc(fgt) | ((uint32_t)__popc(feq) << 16);
-  uint32_t tot;
-  const uint32_t ex = block_exclusive_scan<NT>(packed, tmp, tot);
-  uint32_t gt = gt_base + (ex & 0xFFFFu), eq = eq_base + (ex >> 16);
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    if ((fgt >> j) & 1u) {
-      emit(gt + min(eq, need_eq), key[j], id[j]);
-      ++gt;
-    } else if ((feq >> j) & 1u) {
-      if (eq < need_eq) emit(gt + eq, key[j], id[j]);
-      ++eq;
-    }
-  }
-  gt_base += tot & 0xFFFFu;
-  eq_base += tot >> 16;
 }
 
+// Whole-source ordered compaction; stops after the batch in which `target`
+// elements are out.  Returns the number emitted (uniform).
 template <int NT, class Src, class Emit>
-__device__ __forceinline__ uint32_t compact(const Src& src, uint32_t P, int pbits, uint32_t need_eq, uint32_t target,
-                           uint32_t* tmp, Emit emit, int start = 0, uint32_t gt0 = 0, uint32_t eq0 = 0) {
+__device__ __forceinline__ uint32_t compact(const Src& src, uint32_t P, int pbits, uint32_t need_eq,
+                                            uint32_t target, uint32_t* tmp, Emit emit) {
   const int shift = 32 - pbits;
-  uint32_t gt_base = gt0, eq_base = eq0;
-  if (gt_base + min(eq_base, need_eq) >= target) return gt_base + min(eq_base, need_eq);
+  uint32_t gt_base = 0, eq_base = 0;
   const int n = src.size();
-  for (int base = start; base < n; base += NT * 4 * kUnr) {
+  for (int base = 0; base < n; base += NT * 4 * kUnr) {
     uint32_t key[kUnr][4];
     int id[kUnr][4];
     bool ok[kUnr][4];
     load_batch<NT>(src, base, key, id, ok);
-#pragma unroll
-    for (int u = 0; u < kUnr; ++u) {
-      if (base + u * NT * 4 >= n) break;              // uniform
-      compact_chunk<NT>(key[u], id[u], ok[u], P, shift, need_eq, tmp, gt_base, eq_base, emit);
-      if (gt_base + min(eq_base, need_eq) >= target) return gt_base + min(eq_base, need_eq);
-    }
+    compact_batch<NT>(key, id, ok, P, shift, need_eq, tmp, gt_base, eq_base, emit);
+    if (gt_base + min(eq_base, need_eq) >= target) break;
   }
   return gt_base + min(eq_base, need_eq);
 }
@@ -293,7 +325,7 @@ constexpr int kRowCap = 8192;
 
 __global__ void __launch_bounds__(kRowNT) topk_row_kernel(TopkArgs a) {
   __shared__ uint32_t hist[kBins1];
-  __shared__ uint32_t tmp[kRowNT / 64];
+  __shared__ uint32_t tmp[kUnr * kRowNT / 64];
   __shared__ BinSel res;
   __shared__ uint32_t lkey[kRowCap];
   __shared__ int lidx[kRowCap];
@@ -322,7 +354,7 @@ __global__ void __launch_bounds__(kRowNT) topk_row_kernel(TopkArgs a) {
   if (m <= (uint32_t)kRowCap) {
     compact<kRowNT>(row, s1.bin, kBins1Bits, s1.cnt, m, tmp,
                     [&](uint32_t slot, uint32_t key, int id) { lkey[slot] = key; lidx[slot] = id; });
-    __syncthreads();
+    lds_barrier();
     const LdsSrc ls{lkey, lidx, (int)m};
     refine_and_emit<kRowNT>(ls, s1.bin, kBins1Bits, need, s1.cnt, hist, tmp, &res, k, to_out);
   } else {
@@ -359,7 +391,7 @@ __global__ void __launch_bounds__(kSplitNT) topk_hist_kernel(TopkArgs a) {
 // its own list region, in index order, and records how many it wrote.
 __global__ void __launch_bounds__(kSplitNT) topk_slice_kernel(TopkArgs a) {
   __shared__ uint32_t hist[kBins1];
-  __shared__ uint32_t tmp[kSplitNT / 64];
+  __shared__ uint32_t tmp[kUnr * kSplitNT / 64];
   __shared__ BinSel res;
 
   const int sl = blockIdx.x, t = blockIdx.y;
@@ -387,7 +419,7 @@ __global__ void __launch_bounds__(kSplitNT) topk_slice_kernel(TopkArgs a) {
   }
 
   load_hist<kSplitNT>(a.hist + (int64_t)t * kBins1, hist);
-  __syncthreads();
+  lds_barrier();
   const BinSel s1 = select_bin<kSplitNT>(hist, kBins1, k, tmp, &res);
 
   if (full) {
@@ -403,18 +435,25 @@ __global__ void __launch_bounds__(kSplitNT) topk_slice_kernel(TopkArgs a) {
     load_batch<kSplitNT>(src, 0, key, id, ok);
   }
 
+  if (sl == 0 && threadIdx.x == 0)
+    reinterpret_cast<uint4*>(a.meta)[t] = make_uint4(s1.bin, s1.above, s1.cnt, 0u);
+
+  // Candidates go to this slice's list; those in the boundary bin also count
+  // their next 11 key bits into the row's second-level histogram (a few
+  // hundred scattered atomics per slice, straight to global memory).
   uint2* mylist = a.lists + ((int64_t)t * a.nslices + sl) * a.slice;
-  auto to_list = [&](uint32_t slot, uint32_t kk, int ii) { mylist[slot] = make_uint2(kk, (uint32_t)ii); };
+  uint32_t* gh2 = a.hist2 + (int64_t)t * kBins1;
+  auto to_list = [&](uint32_t slot, uint32_t kk, int ii) {
+    mylist[slot] = make_uint2(kk, (uint32_t)ii);
+    if ((kk >> (32 - kBins1Bits)) == s1.bin) atomicAdd(gh2 + ((kk >> (32 - 2 * kBins1Bits)) & (kBins1 - 1)), 1u);
+  };
   uint32_t gt = 0, eq = 0;
-#pragma unroll
-  for (int u = 0; u < kUnr; ++u) {
-    if (u * kSplitNT * 4 >= src.size()) break;       // uniform
-    compact_chunk<kSplitNT>(key[u], id[u], ok[u], s1.bin, 32 - kBins1Bits, 0xFFFFFFFFu, tmp, gt, eq, to_list);
+  compact_batch<kSplitNT>(key, id, ok, s1.bin, 32 - kBins1Bits, 0xFFFFFFFFu, tmp, gt, eq, to_list);
+  for (int base = kFirst; base < src.size(); base += kFirst) {     // slices longer than one batch
+    load_batch<kSplitNT>(src, base, key, id, ok);
+    compact_batch<kSplitNT>(key, id, ok, s1.bin, 32 - kBins1Bits, 0xFFFFFFFFu, tmp, gt, eq, to_list);
   }
-  const uint32_t mycnt = src.size() > kFirst
-      ? compact<kSplitNT>(src, s1.bin, kBins1Bits, 0xFFFFFFFFu, 0xFFFFFFFFu, tmp, to_list, kFirst, gt, eq)
-      : gt + eq;
-  if (threadIdx.x == 0) a.slice_cnt[(int64_t)t * a.nslices + sl] = mycnt;
+  if (threadIdx.x == 0) a.slice_cnt[(int64_t)t * a.nslices + sl] = gt + eq;
 }
 
 // Phase 2 of split mode (next launch, so every slice's list is visible): one
@@ -422,7 +461,7 @@ __global__ void __launch_bounds__(kSplitNT) topk_slice_kernel(TopkArgs a) {
 // order), refines the boundary bin and emits the selection.
 __global__ void __launch_bounds__(kFinalNT) topk_finalize_kernel(TopkArgs a) {
   __shared__ uint32_t hist[kBins1];
-  __shared__ uint32_t tmp[kFinalNT / 64];
+  __shared__ uint32_t tmp[kUnr * kFinalNT / 64];
   __shared__ BinSel res;
   __shared__ uint32_t lkey[kSplitCap];
   __shared__ int lidx[kSplitCap];
@@ -435,9 +474,10 @@ __global__ void __launch_bounds__(kFinalNT) topk_finalize_kernel(TopkArgs a) {
   const int n = pos + 1;
   const uint32_t k = (uint32_t)a.k;
   if (n <= a.k) return;                         // phase 1 wrote the identity selection
-  load_hist<kFinalNT>(a.hist + (int64_t)t * kBins1, hist);
+  load_hist<kFinalNT>(a.hist2 + (int64_t)t * kBins1, hist);
+  const uint4 s1 = reinterpret_cast<const uint4*>(a.meta)[t];   // first-pass bin, above, count
   if (threadIdx.x < a.nslices) cnt[threadIdx.x] = a.slice_cnt[(int64_t)t * a.nslices + threadIdx.x];
-  __syncthreads();
+  lds_barrier();
   if (threadIdx.x == 0) {
     uint32_t o = 0;
     for (int s = 0; s < a.nslices; ++s) {
@@ -446,9 +486,19 @@ __global__ void __launch_bounds__(kFinalNT) topk_finalize_kernel(TopkArgs a) {
     }
     offs[a.nslices] = o;
   }
-  const BinSel s1 = select_bin<kFinalNT>(hist, kBins1, k, tmp, &res);   // its barriers publish offs
+  // second level: the 11 key bits after the first-pass bin, histogrammed by
+  // the slices over the boundary-bin elements (its barriers publish offs)
+  uint32_t need = k - s1.y;
+  uint32_t P = s1.x, cnt_p = s1.z;
+  int pbits = kBins1Bits;
+  const BinSel s2 = select_bin<kFinalNT>(hist, kBins1, need, tmp, &res);
+  if (cnt_p != need) {
+    P = (P << kBins1Bits) | s2.bin;
+    pbits = 2 * kBins1Bits;
+    need -= s2.above;
+    cnt_p = s2.cnt;
+  }
   const uint32_t m = offs[a.nslices];
-  const uint32_t need = k - s1.above;
   int32_t* out = a.idx + (int64_t)t * a.k;
   auto to_out = [&](uint32_t slot, uint32_t, int id) { out[slot] = id; };
   const uint2* rowlists = a.lists + (int64_t)t * a.nslices * a.slice;
@@ -471,11 +521,11 @@ __global__ void __launch_bounds__(kFinalNT) topk_finalize_kernel(TopkArgs a) {
           }
         }
     }
-    __syncthreads();
+    lds_barrier();
     const LdsSrc ls{lkey, lidx, (int)m};
-    refine_and_emit<kFinalNT>(ls, s1.bin, kBins1Bits, need, s1.cnt, hist, tmp, &res, k, to_out);
+    refine_and_emit<kFinalNT>(ls, P, pbits, need, cnt_p, hist, tmp, &res, k, to_out);
   } else {
-    refine_and_emit<kFinalNT>(gs, s1.bin, kBins1Bits, need, s1.cnt, hist, tmp, &res, k, to_out);
+    refine_and_emit<kFinalNT>(gs, P, pbits, need, cnt_p, hist, tmp, &res, k, to_out);
   }
 }
 
