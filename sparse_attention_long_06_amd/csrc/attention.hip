@@ -16,7 +16,8 @@
 //   * S^T = K q^T: v_mfma_f32_16x16x32_bf16 with M = 16 selected rows, N = 16
 //     heads, K = 32 dims; K comes from the tile (ds_read_b128), q sits in
 //     registers.  Lane l ends with head (l%16) and rows 4*(l/16)+i.
-//   * online softmax in log2 units; P rounded to bf16.
+//   * online softmax in log2 units with a lazily moved reference max (P <
+//     2^8, O rescaled only when a block max jumps past it); P rounded to bf16.
 //   * O += P V: M = 16 heads, N = 16 value dims, K = 32 rows.  The S^T
 //     accumulator of row tiles 2kb and 2kb+1 is this MFMA's A operand when K
 //     slot j of lane group g stands for row 32kb+4g+j (j<4) or 32kb+16+4g+j-4.
@@ -217,9 +218,15 @@ __global__ void __launch_bounds__(512) attn_kernel(AttnArgs a) {
       }
       mx = fmaxf(mx, __shfl_xor(mx, 16));
       mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = fmaxf(m_run[ht], mx);
-      const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
-      alpha[ht] = __builtin_amdgcn_exp2f(m_run[ht] - m_use);
+      // Lazy rescaling: the reference max moves only when the block max
+      // exceeds it by more than 8 (log2 units), so P stays below 2^8 and the
+      // O accumulators are rescaled rarely instead of on most blocks.  While
+      // nothing valid has been seen, the reference is -inf and O is zero.
+      const float m_old = m_run[ht];
+      const bool move = mx > m_old + 8.0f;
+      const float m_ref = move ? mx : m_old;
+      const float m_use = (m_ref == -INFINITY) ? 0.0f : m_ref;
+      alpha[ht] = (move && m_old != -INFINITY) ? __builtin_amdgcn_exp2f(m_old - m_ref) : 1.0f;
       float psum = 0.0f;
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
@@ -231,7 +238,7 @@ __global__ void __launch_bounds__(512) attn_kernel(AttnArgs a) {
         }
       }
       l_run[ht] = l_run[ht] * alpha[ht] + psum;
-      m_run[ht] = m_new;
+      m_run[ht] = m_ref;
     }
 
     // rescale O (lane holds heads 4*grp+i of each tile): fetch alpha of those heads
