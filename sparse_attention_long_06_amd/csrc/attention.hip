@@ -327,7 +327,12 @@ __global__ void __launch_bounds__(512) attn_kernel(AttnArgs a) {
 }
 
 // Merge split partials: lse = log sum_i exp(lse_i); out = sum_i exp(lse_i - lse) O_i.
-// One thread per 8 consecutive value dims of one head.
+// One thread per 8 consecutive value dims of one head.  The partials are read
+// in groups of kCombineGroup splits whose loads are all issued before any is
+// used; the weights are taken relative to the largest split lse and the sum
+// is normalised once at the end.
+constexpr int kCombineGroup = 8;
+
 __global__ void __launch_bounds__(256) attn_combine_kernel(CombineArgs a) {
   const int per_head = a.D_v / 8;
   // same XCD-major order as the attention workgroups that wrote the partials
@@ -339,22 +344,45 @@ __global__ void __launch_bounds__(256) attn_combine_kernel(CombineArgs a) {
   const int h = (int)(th % a.H);
   const int t = (int)(th / a.H);
   const float* pl = a.part_lse + (int64_t)t * a.nsplit * a.H + h;
-  float mx = -INFINITY;
-  for (int i = 0; i < a.nsplit; ++i) mx = fmaxf(mx, pl[(int64_t)i * a.H]);
+  const uint16_t* po = a.part_o + ((int64_t)t * a.nsplit * a.H + h) * a.D_v + d8 * 8;
+  const int64_t po_stride = (int64_t)a.H * a.D_v;
+  // one pass: each group's lse values and partials are loaded together; the
+  // running reference (largest lse so far) rescales the sums when it moves
+  float mx = -INFINITY, den = 0.0f;
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int g = 0; g < a.nsplit; g += kCombineGroup) {
+    float wl[kCombineGroup];
+    v4i raw[kCombineGroup];
+#pragma unroll
+    for (int j = 0; j < kCombineGroup; ++j) {
+      const bool v = g + j < a.nsplit;
+      wl[j] = v ? pl[(int64_t)(g + j) * a.H] : -INFINITY;
+      raw[j] = v ? *reinterpret_cast<const v4i*>(po + (g + j) * po_stride) : v4i{0, 0, 0, 0};
+    }
+    float gm = mx;
+#pragma unroll
+    for (int j = 0; j < kCombineGroup; ++j) gm = fmaxf(gm, wl[j]);
+    if (gm == -INFINITY) continue;                  // nothing valid yet
+    const float sc = __expf(mx - gm);               // 0 while mx is -inf
+    den *= sc;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] *= sc;
+    mx = gm;
+#pragma unroll
+    for (int j = 0; j < kCombineGroup; ++j) {
+      const float wgt = __expf(wl[j] - mx);
+      den += wgt;
+      const v8bf pv = __builtin_bit_cast(v8bf, raw[j]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] += wgt * (float)pv[e];
+    }
+  }
   float lse = -INFINITY;
   if (mx != -INFINITY) {
-    float den = 0.0f;
-    for (int i = 0; i < a.nsplit; ++i) den += __expf(pl[(int64_t)i * a.H] - mx);
     lse = mx + __logf(den);
-    for (int i = 0; i < a.nsplit; ++i) {
-      const float wgt = __expf(pl[(int64_t)i * a.H] - lse);
-      const v4i raw = *reinterpret_cast<const v4i*>(
-          a.part_o + (((int64_t)t * a.nsplit + i) * a.H + h) * a.D_v + d8 * 8);
-      const v8bf pv = __builtin_bit_cast(v8bf, raw);
+    const float inv = 1.0f / den;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) acc[j] += wgt * (float)pv[j];
-    }
+    for (int e = 0; e < 8; ++e) acc[e] *= inv;
   }
   uint32_t pk[4];
 #pragma unroll
