@@ -97,9 +97,12 @@ def run_bench(args):
         raise SystemExit(f"bench.py times the decode path; {wl.name} is a {wl.kind} workload")
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    print(f"[bench] generating {wl.name} on {dev}", file=sys.stderr, flush=True)
-    inp = W.generate(wl, dev)
-    batch = dsa.Batch.from_inputs(inp)
+    # Two copies of the inputs at different addresses, used on alternate
+    # steps, so no step finds the previous step's keys in the caches.
+    print(f"[bench] generating {wl.name} on {dev} (2 copies)", file=sys.stderr, flush=True)
+    sets = [W.generate(wl, dev) for _ in range(2)]
+    batches = [dsa.Batch.from_inputs(x) for x in sets]
+    inp, batch = sets[0], batches[0]
     B = inp.num_rows
     out = torch.empty((B, wl.H, wl.D_v), dtype=torch.bfloat16, device=dev)
     lse = torch.empty((B, wl.H), dtype=torch.float32, device=dev)
@@ -108,56 +111,88 @@ def run_bench(args):
     ws = torch.empty(ws_n, dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
 
-    def step():
-        dsa.decode(batch, inp.q8, inp.q_scale, inp.w, inp.k8, inp.k_scale, wl.k, inp.q, inp.kv, inp.v,
+    def step(i):
+        x, bt = sets[i % 2], batches[i % 2]
+        dsa.decode(bt, x.q8, x.q_scale, x.w, x.k8, x.k_scale, wl.k, x.q, x.kv, x.v,
                    wl.scale, out=out, lse=lse, idx_out=idx, workspace=ws, D_v=wl.D_v)
 
     print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
-    for _ in range(args.warmup):
-        step()
+    for i in range(args.warmup):
+        step(i)
     torch.cuda.synchronize()
 
-    # stage events for every timed step (recorded by the library on its stream)
+    # Four stage events per timed step, recorded by the library on its stream
+    # around the indexer (0, 1), after the top-k (2) and at the end (3).
+    NEV = 4
     hip = _hip()
     lib = _lib.load()
     events = []
-    for _ in range(4 * args.steps):
+    for _ in range(NEV * args.steps):
         ev = ctypes.c_void_p()
         assert hip.hipEventCreate(ctypes.byref(ev)) == 0
         events.append(ev.value)
-    step_events = [(ctypes.c_void_p * 4)(*events[4 * i: 4 * i + 4]) for i in range(args.steps)]
+    step_events = [(ctypes.c_void_p * NEV)(*events[NEV * i: NEV * i + NEV]) for i in range(args.steps)]
 
     print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        assert lib.dsa_set_stage_events(step_events[i], 4) == 0
-        step()
+        assert lib.dsa_set_stage_events(step_events[i], NEV) == 0
+        step(i)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     elapsed = t1 - t0
 
-    stage_ms = {"indexer": 0.0, "topk": 0.0, "attention": 0.0}
     f = ctypes.c_float()
+
+    def ev_ms(e, a, b):
+        assert hip.hipEventElapsedTime(ctypes.byref(f), ctypes.c_void_p(e[a]), ctypes.c_void_p(e[b])) == 0
+        return f.value
+
+    stage_ms = {"indexer": 0.0, "topk": 0.0, "attention": 0.0}
     for i in range(args.steps):
-        e = events[4 * i: 4 * i + 4]
+        e = events[NEV * i: NEV * i + NEV]
         for name, (a, b) in zip(stage_ms, [(0, 1), (1, 2), (2, 3)]):
-            assert hip.hipEventElapsedTime(ctypes.byref(f), ctypes.c_void_p(e[a]), ctypes.c_void_p(e[b])) == 0
-            stage_ms[name] += f.value / args.steps
+            stage_ms[name] += ev_ms(e, a, b) / args.steps
     for ev in events:
         hip.hipEventDestroy(ctypes.c_void_p(ev))
 
+    lens = inp.seq_lens_host
+    idx_bytes = sum(decode_bytes_per_query(wl, L)[0] for L in lens)
+    other_bytes = sum(decode_bytes_per_query(wl, L)[1] for L in lens)
+    idx_gbs = idx_bytes / (stage_ms["indexer"] * 1e-3) / 1e9
+
+    # The three entry points called one by one through the binding (after the
+    # timed steps), for reference next to the in-step stage times above.
+    print("[bench] per-stage calls", file=sys.stderr, flush=True)
+    scores = torch.empty((B, (inp.max_len + 3) // 4 * 4), dtype=torch.float32, device=dev)
+
+    def timed(fn, reps=10):
+        fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            e1.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        return sorted(ts)[len(ts) // 2]
+
+    st_ix = timed(lambda: dsa.indexer(batch, inp.q8, inp.q_scale, inp.w, inp.k8, inp.k_scale, scores=scores))
+    st_tk = timed(lambda: dsa.topk(batch, scores, wl.k, idx=idx))
+    st_at = timed(lambda: dsa.sparse_attn(batch, inp.q, inp.kv, inp.v, wl.scale, idx, out=out, lse=lse, D_v=wl.D_v))
+    del scores
+
     ms = elapsed * 1e3 / args.steps
     qps = B / (elapsed / args.steps)
-    ctx_total = sum(inp.seq_lens_host)
-    idx_bytes = sum(decode_bytes_per_query(wl, L)[0] for L in inp.seq_lens_host)
-    other_bytes = sum(decode_bytes_per_query(wl, L)[1] for L in inp.seq_lens_host)
-    idx_gbs = idx_bytes / (stage_ms["indexer"] * 1e-3) / 1e9
+    ctx_total = sum(lens)
     step_gbs = (idx_bytes + other_bytes) / (ms * 1e-3) / 1e9
     att_bytes = other_bytes - B * (wl.H_I * wl.d_I + wl.H_I * 4 + 4)
     att_gbs = att_bytes / (stage_ms["attention"] * 1e-3) / 1e9
-    att_flops = sum(2 * wl.H * min(wl.k, L) * (wl.D + wl.D_v) for L in inp.seq_lens_host)
-    idx_flops = sum(2 * wl.H_I * wl.d_I * L for L in inp.seq_lens_host)
+    att_flops = sum(2 * wl.H * min(wl.k, L) * (wl.D + wl.D_v) for L in lens)
+    idx_flops = sum(2 * wl.H_I * wl.d_I * L for L in lens)
 
     res = {
         "metric": "DSA decode queries/s @128K ctx, k=2048; indexer TFLOPS + attn HBM GB/s",
@@ -171,7 +206,8 @@ def run_bench(args):
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "fp8-storage/bf16-mfma",
-        "data": "synthetic (seeded N(0,1) draws, per-token e4m3fn quantised indexer q/k; bf16 latent KV)",
+        "data": "synthetic (seeded N(0,1) draws, per-token e4m3fn quantised indexer q/k; bf16 latent KV; "
+                "two input copies used on alternate steps)",
         "config": {"workload": wl.name, "queries": B, "context": wl.seq_len, "k": wl.k, "H_I": wl.H_I,
                    "d_I": wl.d_I, "H": wl.H, "D": wl.D, "D_v": wl.D_v, "paged": wl.paged,
                    "parallelism": "single GPU"},
@@ -182,11 +218,14 @@ def run_bench(args):
                      "frac": round(idx_gbs / HBM_PEAK_GBS, 4), "traffic": indexer_traffic_bytes(),
                      "bytes_per_launch": idx_bytes, "launch_ms": round(stage_ms["indexer"], 4)},
         "stages_ms": {k: round(v, 4) for k, v in stage_ms.items()},
+        "stages_separate_calls_ms": {"indexer": round(st_ix, 4), "topk": round(st_tk, 4),
+                                     "attention": round(st_at, 4)},
         "step_hbm": {"bytes": idx_bytes + other_bytes, "GB/s": round(step_gbs, 1),
                      "frac": round(step_gbs / HBM_PEAK_GBS, 4)},
         "indexer_tflops": round(idx_flops / (stage_ms["indexer"] * 1e-3) / 1e12, 2),
         "attention": {"GB/s": round(att_gbs, 1), "hbm_frac": round(att_gbs / HBM_PEAK_GBS, 4),
-                      "TFLOP/s": round(att_flops / (stage_ms["attention"] * 1e-3) / 1e12, 2)},
+                      "TFLOP/s": round(att_flops / (stage_ms["attention"] * 1e-3) / 1e12, 2),
+                      "bf16_frac": round(att_flops / (stage_ms["attention"] * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)},
     }
     del ws, out, lse
     return res, inp
