@@ -36,9 +36,9 @@ BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, vendor figure
 INDEXER_COUNTERS = {
     "sources": ["sparse_attention_long_06_amd/csrc/indexer.hip", "sparse_attention_long_06_amd/csrc/dsa_common.h",
                 "sparse_attention_long_06_amd/csrc/dsa_kernels.h", "sparse_attention_long_06_amd/csrc/api.hip"],
-    "sha256": None,
-    "fetch_kib": None,
-    "write_kib": None,
+    "sha256": "e1e28f1a1c638d33507bc68044dd17dcf7e69ccb0acb5c5cb2f3a05435b39bb1",
+    "fetch_kib": 272629.0,
+    "write_kib": 17231.2,
     "fetch_scale": 2.0,
     "write_scale": 1.0,
 }
