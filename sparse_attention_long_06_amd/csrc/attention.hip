@@ -104,6 +104,21 @@ __global__ void __launch_bounds__(512) attn_kernel(AttnArgs a) {
   const int nl = lane & 15, grp = lane >> 4;
   const int h0 = wave * 16 * HW;
 
+  // q fragments (B operand of S^T): head h0+16*ht+nl, dims 32*kk + 8*grp .. +7.
+  // Requested first: they depend on nothing, so their latency overlaps the
+  // sequence-length and index loads below instead of following them.
+  v8bf qf[HW][KK];
+#pragma unroll
+  for (int ht = 0; ht < HW; ++ht) {
+    const int h = h0 + ht * 16 + nl;
+    const bool ok = h < a.H;
+    const uint16_t* qrow = a.q + ((int64_t)t * a.H + (ok ? h : 0)) * D;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      const v4i raw = ok ? *reinterpret_cast<const v4i*>(qrow + kk * 32 + grp * 8) : v4i{0, 0, 0, 0};
+      qf[ht][kk] = __builtin_bit_cast(v8bf, raw);
+    }
+  }
   int b, pos;
   row_seq_pos(a.g, t, b, pos);
   const int slot_beg = split * a.per_split;
@@ -123,19 +138,6 @@ __global__ void __launch_bounds__(512) attn_kernel(AttnArgs a) {
     if constexpr (SEPV) vrowid[i] = s >= 0 ? (uint32_t)token_row(a.g, a.v, b, s) : vfallback;
   }
 
-  // q fragments (B operand of S^T): head h0+16*ht+nl, dims 32*kk + 8*grp .. +7
-  v8bf qf[HW][KK];
-#pragma unroll
-  for (int ht = 0; ht < HW; ++ht) {
-    const int h = h0 + ht * 16 + nl;
-    const bool ok = h < a.H;
-    const uint16_t* qrow = a.q + ((int64_t)t * a.H + (ok ? h : 0)) * D;
-#pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
-      const v4i raw = ok ? *reinterpret_cast<const v4i*>(qrow + kk * 32 + grp * 8) : v4i{0, 0, 0, 0};
-      qf[ht][kk] = __builtin_bit_cast(v8bf, raw);
-    }
-  }
   __syncthreads();
 
   v4f o[HW][NT];
