@@ -17,8 +17,8 @@
  *                        per token (same article, same section; degnora.com
  *                        "DeepSeekV3, Farkı Ne?", section "MLA — Multi-Latent
  *                        Attention").
- *   dsa_decode chains the three for one query per sequence without any host
- *   round trip between the stages (sider.ai "Sparse attention that isn't
+ *   dsa_decode (one query per sequence) and dsa_prefill (query rows per
+ *   sequence) chain the three without any host round trip between the stages (sider.ai "Sparse attention that isn't
  *   sparse thinking", sections "Uyarılar" and "Dağıtım Gerçekliği": selection
  *   that bounces between CPU and GPU, or launch overhead, eats the gain).
  *
@@ -145,7 +145,13 @@ dsa_status dsa_sparse_attn(const dsa_batch* batch, const uint16_t* q, const dsa_
  * NULL), enqueued back to back with no host synchronisation: indexer scores
  * (kept in the workspace), top-k, sparse attention.
  * Arguments as in the three calls above; idx_out [B, k] receives the
- * selected indices when not NULL.
+ * selected indices when not NULL.  Workspace: dsa_workspace_size(
+ * DSA_WS_DECODE, ...) bytes, 256-byte aligned.
+ * Short contexts: when batch->max_len <= k every query selects all of its
+ * tokens (the selection is then independent of the scores), so the indexer
+ * is skipped, the identity selections are written and the attention is
+ * dense (tenelement.pl article, "Architektura DeepSeek V3.2-Exp: Od MoE do
+ * DSA": dense attention at short lengths).
  */
 dsa_status dsa_decode(const dsa_batch* batch, const uint8_t* q8, const float* q_scale,
                       const float* w, const dsa_cache* kidx, const dsa_cache* kscale,
@@ -155,10 +161,28 @@ dsa_status dsa_decode(const dsa_batch* batch, const uint8_t* q8, const float* q_
                       void* workspace, size_t ws_bytes, void* stream);
 
 /*
- * dsa_set_stage_events — opt-in stage timing for the NEXT dsa_decode call on
+ * dsa_prefill — the same fused path for a batch of query rows per sequence
+ * (q_start must be set): indexer over every causal (row, token) pair, top-k,
+ * sparse attention, on one stream.  Arguments as in dsa_decode; out, lse and
+ * idx_out have num_rows rows.  Workspace: dsa_workspace_size(
+ * DSA_WS_PREFILL, ...) bytes, 256-byte aligned (it holds the [num_rows,
+ * max_len] score matrix).  The short-context shortcut of dsa_decode applies:
+ * with max_len <= k no scores are computed and the attention is dense causal.
+ * Errors: as dsa_decode; DSA_ERR_SHAPE when q_start is NULL.
+ */
+dsa_status dsa_prefill(const dsa_batch* batch, const uint8_t* q8, const float* q_scale,
+                       const float* w, const dsa_cache* kidx, const dsa_cache* kscale,
+                       int H_I, int d_I, int k, const uint16_t* q, const dsa_cache* kv,
+                       const dsa_cache* v, int H, int D, int D_v, float scale,
+                       uint16_t* out, float* lse, int32_t* idx_out,
+                       void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * dsa_set_stage_events — opt-in stage timing for the NEXT dsa_decode or
+ * dsa_prefill call on
  * this thread (for profiling tools; the stages are the ones the pages name:
  * indexer, selection, core attention).  `events` holds `count` >= 4 hipEvent_t
- * handles created by the caller; dsa_decode records them on its stream:
+ * handles created by the caller; that call records them on its stream:
  *   events[0] before the indexer (after the workspace clear),
  *   events[1] after the indexer, events[2] after the top-k,
  *   events[3] after the attention (and its split combine).
@@ -169,11 +193,11 @@ dsa_status dsa_decode(const dsa_batch* batch, const uint8_t* q8, const float* q_
 dsa_status dsa_set_stage_events(void* const* events, int count);
 
 /* Which call dsa_workspace_size() sizes. */
-enum { DSA_WS_TOPK = 1, DSA_WS_ATTN = 2, DSA_WS_DECODE = 3 };
+enum { DSA_WS_TOPK = 1, DSA_WS_ATTN = 2, DSA_WS_DECODE = 3, DSA_WS_PREFILL = 4 };
 
 /*
  * Workspace bytes `entry` needs for this batch (host-only; no device call).
- * H and D_v matter for DSA_WS_ATTN / DSA_WS_DECODE only.  Returns 0 when the
+ * H and D_v matter for DSA_WS_ATTN / DSA_WS_DECODE / DSA_WS_PREFILL only.  Returns 0 when the
  * call needs none, and (size_t)-1 for invalid arguments.
  */
 size_t dsa_workspace_size(int entry, const dsa_batch* batch, int k, int H, int D_v);

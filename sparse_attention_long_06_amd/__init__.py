@@ -20,7 +20,7 @@ from typing import Optional
 import torch
 
 from . import _lib
-from ._lib import DSA_WS_ATTN, DSA_WS_DECODE, DSA_WS_TOPK, DsaBatch, DsaCache  # noqa: F401
+from ._lib import DSA_WS_ATTN, DSA_WS_DECODE, DSA_WS_PREFILL, DSA_WS_TOPK, DsaBatch, DsaCache  # noqa: F401
 
 __all__ = ["Batch", "DsaError", "indexer", "topk", "sparse_attn", "decode", "workspace_size", "cache_view"]
 
@@ -159,9 +159,8 @@ def sparse_attn(batch: Batch, q, kv, v, scale: float, idx, out=None, lse=None, D
     return out, lse
 
 
-def decode(batch: Batch, q8, q_scale, w, k8, k_scale, k: int, q, kv, v, scale: float,
+def _fused(entry: str, ws_kind: int, batch: Batch, q8, q_scale, w, k8, k_scale, k: int, q, kv, v, scale: float,
            out=None, lse=None, idx_out=None, workspace=None, D_v: Optional[int] = None):
-    """Whole path for one query per sequence; returns (out, lse, idx_out)."""
     lib = _lib.load()
     T, H, D = (int(x) for x in q.shape)
     H_I, d_I = int(q8.shape[1]), int(q8.shape[2])
@@ -172,7 +171,7 @@ def decode(batch: Batch, q8, q_scale, w, k8, k_scale, k: int, q, kv, v, scale: f
         out = torch.empty((T, H, D_v), dtype=torch.bfloat16, device=dev)
     if lse is None:
         lse = torch.empty((T, H), dtype=torch.float32, device=dev)
-    ws_n = workspace_size(DSA_WS_DECODE, batch, k, H, D_v)
+    ws_n = workspace_size(ws_kind, batch, k, H, D_v)
     if workspace is None:
         workspace = _workspace(ws_n, dev)
     elif workspace.numel() < ws_n:
@@ -180,7 +179,22 @@ def decode(batch: Batch, q8, q_scale, w, k8, k_scale, k: int, q, kv, v, scale: f
     b = batch.c()
     kc, sc = cache_view(k8, batch), cache_view(k_scale, batch)
     kvc, vc = cache_view(kv, batch), cache_view(v, batch)
-    _check(lib.dsa_decode(ctypes.byref(b), _ptr(q8), _ptr(q_scale), _ptr(w), _ref(kc), _ref(sc), H_I, d_I, k,
-                          _ptr(q), _ref(kvc), _ref(vc), H, D, D_v, float(scale), _ptr(out), _ptr(lse), _ptr(idx_out),
-                          _ptr(workspace), ws_n if workspace is not None else 0, _stream(dev)), "dsa_decode")
+    _check(getattr(lib, entry)(ctypes.byref(b), _ptr(q8), _ptr(q_scale), _ptr(w), _ref(kc), _ref(sc), H_I, d_I, k,
+                               _ptr(q), _ref(kvc), _ref(vc), H, D, D_v, float(scale), _ptr(out), _ptr(lse),
+                               _ptr(idx_out), _ptr(workspace), ws_n if workspace is not None else 0, _stream(dev)),
+           entry)
     return out, lse, idx_out
+
+
+def decode(batch: Batch, q8, q_scale, w, k8, k_scale, k: int, q, kv, v, scale: float,
+           out=None, lse=None, idx_out=None, workspace=None, D_v: Optional[int] = None):
+    """Whole path for one query per sequence (dsa_decode); returns (out, lse, idx_out)."""
+    return _fused("dsa_decode", DSA_WS_DECODE, batch, q8, q_scale, w, k8, k_scale, k, q, kv, v, scale,
+                  out, lse, idx_out, workspace, D_v)
+
+
+def prefill(batch: Batch, q8, q_scale, w, k8, k_scale, k: int, q, kv, v, scale: float,
+            out=None, lse=None, idx_out=None, workspace=None, D_v: Optional[int] = None):
+    """Whole path for query rows per sequence (dsa_prefill); returns (out, lse, idx_out)."""
+    return _fused("dsa_prefill", DSA_WS_PREFILL, batch, q8, q_scale, w, k8, k_scale, k, q, kv, v, scale,
+                  out, lse, idx_out, workspace, D_v)

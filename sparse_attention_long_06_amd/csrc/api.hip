@@ -165,23 +165,29 @@ AttnPlan plan_attn(int T, int k, int H, int D_v) {
   return p;
 }
 
-struct DecodePlan {
+// Workspace of the fused entry points (dsa_decode, dsa_prefill) over T query
+// rows.  When every row sees at most k tokens (max_len <= k) the selection is
+// every prior token: no scores, no indexer, and the top-k launch only writes
+// the identity lists.
+struct FusedPlan {
+  bool dense = false;
   int64_t ld = 0;
   TopkPlan tk;
   AttnPlan at;
   size_t off_scores = 0, off_topk = 0, off_idx = 0, off_attn = 0, bytes = 0;
 };
 
-DecodePlan plan_decode(int B, int max_len, int k, int H, int D_v) {
-  DecodePlan p;
-  p.ld = round_up(max_len, 4);
-  p.tk = plan_topk(B, max_len, k);
-  p.at = plan_attn(B, k, H, D_v);
+FusedPlan plan_fused(int T, int max_len, int k, int H, int D_v) {
+  FusedPlan p;
+  p.dense = max_len <= k;
+  p.ld = p.dense ? 0 : round_up(max_len, 4);
+  if (!p.dense) p.tk = plan_topk(T, max_len, k);
+  p.at = plan_attn(T, k, H, D_v);
   size_t o = 0;
-  p.off_scores = o; o += (size_t)B * p.ld * 4;
+  p.off_scores = o; o += (size_t)T * p.ld * 4;
   o = (size_t)round_up((int64_t)o, 256);
   p.off_topk = o; o += p.tk.bytes;
-  p.off_idx = o; o += (size_t)round_up((int64_t)B * k * 4, 256);
+  p.off_idx = o; o += (size_t)round_up((int64_t)T * k * 4, 256);
   p.off_attn = o; o += p.at.bytes;
   p.bytes = o;
   return p;
@@ -351,7 +357,10 @@ extern "C" size_t dsa_workspace_size(int entry, const dsa_batch* batch, int k, i
       return plan_attn(batch->num_rows, k, H, D_v).bytes;
     case DSA_WS_DECODE:
       if (H < 1 || D_v < 1 || batch->q_start) return (size_t)-1;
-      return plan_decode(batch->num_seqs, batch->max_len, k, H, D_v).bytes;
+      return plan_fused(batch->num_rows, batch->max_len, k, H, D_v).bytes;
+    case DSA_WS_PREFILL:
+      if (H < 1 || D_v < 1 || !batch->q_start) return (size_t)-1;
+      return plan_fused(batch->num_rows, batch->max_len, k, H, D_v).bytes;
     default:
       return (size_t)-1;
   }
@@ -413,6 +422,63 @@ extern "C" dsa_status dsa_sparse_attn(const dsa_batch* batch, const uint16_t* q,
   return st == DSA_OK ? ok() : st;
 }
 
+namespace {
+
+// The fused path over all rows of the batch, enqueued on one stream:
+// [workspace clear] -> indexer -> top-k -> attention (+ split combine), or,
+// when no row sees more than k tokens, identity selections -> attention.
+// One query per sequence (decode) gets the first top-k histogram from the
+// indexer; other batches build it in the top-k step.
+dsa_status run_fused(const dsa_batch* batch, const uint8_t* q8, const float* q_scale, const float* w,
+                     const dsa_cache* kidx, const dsa_cache* kscale, int H_I, int d_I, int k, const uint16_t* q,
+                     const dsa_cache* kv, const dsa_cache* v, int H, int D, int D_v, float scale, uint16_t* out,
+                     float* lse, int32_t* idx_out, const FusedPlan& p, char* ws, hipStream_t s) {
+  float* scores = reinterpret_cast<float*>(ws + p.off_scores);
+  char* tws = ws + p.off_topk;
+  int32_t* idx = idx_out ? idx_out : reinterpret_cast<int32_t*>(ws + p.off_idx);
+  const bool timed = g_stage_armed;
+  g_stage_armed = false;
+  auto mark = [&](int i) -> hipError_t { return timed ? hipEventRecord(g_stage_events[i], s) : hipSuccess; };
+  const bool decode = batch->q_start == nullptr;
+  uint32_t* hist = nullptr;
+  if (!p.dense && decode && p.tk.split) {
+    hist = reinterpret_cast<uint32_t*>(tws + p.tk.off_hist);
+    LAUNCH(launch_zero(hist, (int64_t)p.tk.zero_words, s), "workspace clear");
+  }
+  LAUNCH(mark(0), "stage event");
+  dsa_status st;
+  if (!p.dense) {
+    st = run_indexer(batch, q8, q_scale, w, kidx, kscale, H_I, d_I, scores, p.ld, hist, s);
+    if (st != DSA_OK) return st;
+  }
+  LAUNCH(mark(1), "stage event");
+  st = run_topk(batch, scores, p.dense ? 4 : p.ld, k, idx, p.tk, tws, hist != nullptr, s);
+  if (st != DSA_OK) return st;
+  LAUNCH(mark(2), "stage event");
+  st = run_attn(batch, q, kv, v, H, D, D_v, scale, idx, k, out, lse, p.at, ws + p.off_attn, s);
+  if (st != DSA_OK) return st;
+  LAUNCH(mark(3), "stage event");
+  return DSA_OK;
+}
+
+dsa_status check_fused(const dsa_batch* batch, const uint8_t* q8, const float* w, const dsa_cache* kidx,
+                       const dsa_cache* kscale, int H_I, int d_I, int k, const uint16_t* q, const dsa_cache* kv,
+                       const dsa_cache* v, int H, int D, int D_v, float scale, uint16_t* out, const FusedPlan& p,
+                       void* workspace, size_t ws_bytes) {
+  dsa_status st = check_indexer_args(batch, q8, w, kidx, kscale, H_I, d_I);
+  if (st != DSA_OK) return st;
+  st = check_attn_args(batch, q, kv, v, H, D, D_v, scale, k);
+  if (st != DSA_OK) return st;
+  CHECK(out, DSA_ERR_NULL, "out is NULL");
+  CHECK(workspace, DSA_ERR_WORKSPACE, "the fused path needs %zu workspace bytes, got NULL", p.bytes);
+  CHECK(ws_bytes >= p.bytes, DSA_ERR_WORKSPACE, "the fused path needs %zu workspace bytes, got %zu", p.bytes,
+        ws_bytes);
+  CHECK(aligned(workspace, 256), DSA_ERR_ALIGN, "workspace not 256-byte aligned");
+  return DSA_OK;
+}
+
+}  // namespace
+
 extern "C" dsa_status dsa_decode(const dsa_batch* batch, const uint8_t* q8, const float* q_scale, const float* w,
                                  const dsa_cache* kidx, const dsa_cache* kscale, int H_I, int d_I, int k,
                                  const uint16_t* q, const dsa_cache* kv, const dsa_cache* v, int H, int D, int D_v,
@@ -421,38 +487,28 @@ extern "C" dsa_status dsa_decode(const dsa_batch* batch, const uint8_t* q8, cons
   dsa_status st = check_batch(batch);
   if (st != DSA_OK) return st;
   CHECK(batch->q_start == nullptr, DSA_ERR_SHAPE, "dsa_decode takes one query per sequence (q_start must be NULL)");
-  st = check_indexer_args(batch, q8, w, kidx, kscale, H_I, d_I);
+  const FusedPlan p = plan_fused(batch->num_rows, batch->max_len, k, H, D_v);
+  st = check_fused(batch, q8, w, kidx, kscale, H_I, d_I, k, q, kv, v, H, D, D_v, scale, out, p, workspace, ws_bytes);
   if (st != DSA_OK) return st;
-  st = check_attn_args(batch, q, kv, v, H, D, D_v, scale, k);
-  if (st != DSA_OK) return st;
-  CHECK(out, DSA_ERR_NULL, "out is NULL");
-  const DecodePlan p = plan_decode(batch->num_seqs, batch->max_len, k, H, D_v);
-  CHECK(workspace, DSA_ERR_WORKSPACE, "decode needs %zu workspace bytes, got NULL", p.bytes);
-  CHECK(ws_bytes >= p.bytes, DSA_ERR_WORKSPACE, "decode needs %zu workspace bytes, got %zu", p.bytes, ws_bytes);
-  CHECK(aligned(workspace, 256), DSA_ERR_ALIGN, "workspace not 256-byte aligned");
+  if (batch->num_rows == 0) return ok();
+  st = run_fused(batch, q8, q_scale, w, kidx, kscale, H_I, d_I, k, q, kv, v, H, D, D_v, scale, out, lse, idx_out, p,
+                 static_cast<char*>(workspace), static_cast<hipStream_t>(stream));
+  return st == DSA_OK ? ok() : st;
+}
 
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  char* ws = static_cast<char*>(workspace);
-  float* scores = reinterpret_cast<float*>(ws + p.off_scores);
-  char* tws = ws + p.off_topk;
-  int32_t* idx = idx_out ? idx_out : reinterpret_cast<int32_t*>(ws + p.off_idx);
-  const bool timed = g_stage_armed;
-  g_stage_armed = false;
-  auto mark = [&](int i) -> hipError_t { return timed ? hipEventRecord(g_stage_events[i], s) : hipSuccess; };
-  uint32_t* hist = nullptr;
-  if (p.tk.split) {
-    hist = reinterpret_cast<uint32_t*>(tws + p.tk.off_hist);
-    LAUNCH(launch_zero(hist, (int64_t)p.tk.zero_words, s), "workspace clear");
-  }
-  LAUNCH(mark(0), "stage event");
-  st = run_indexer(batch, q8, q_scale, w, kidx, kscale, H_I, d_I, scores, p.ld, hist, s);
+extern "C" dsa_status dsa_prefill(const dsa_batch* batch, const uint8_t* q8, const float* q_scale, const float* w,
+                                  const dsa_cache* kidx, const dsa_cache* kscale, int H_I, int d_I, int k,
+                                  const uint16_t* q, const dsa_cache* kv, const dsa_cache* v, int H, int D, int D_v,
+                                  float scale, uint16_t* out, float* lse, int32_t* idx_out, void* workspace,
+                                  size_t ws_bytes, void* stream) {
+  dsa_status st = check_batch(batch);
   if (st != DSA_OK) return st;
-  LAUNCH(mark(1), "stage event");
-  st = run_topk(batch, scores, p.ld, k, idx, p.tk, tws, true, s);
+  CHECK(batch->q_start != nullptr, DSA_ERR_SHAPE, "dsa_prefill takes query rows per sequence (q_start must be set)");
+  const FusedPlan p = plan_fused(batch->num_rows, batch->max_len, k, H, D_v);
+  st = check_fused(batch, q8, w, kidx, kscale, H_I, d_I, k, q, kv, v, H, D, D_v, scale, out, p, workspace, ws_bytes);
   if (st != DSA_OK) return st;
-  LAUNCH(mark(2), "stage event");
-  st = run_attn(batch, q, kv, v, H, D, D_v, scale, idx, k, out, lse, p.at, ws + p.off_attn, s);
-  if (st != DSA_OK) return st;
-  LAUNCH(mark(3), "stage event");
-  return ok();
+  if (batch->num_rows == 0) return ok();
+  st = run_fused(batch, q8, q_scale, w, kidx, kscale, H_I, d_I, k, q, kv, v, H, D, D_v, scale, out, lse, idx_out, p,
+                 static_cast<char*>(workspace), static_cast<hipStream_t>(stream));
+  return st == DSA_OK ? ok() : st;
 }

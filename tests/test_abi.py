@@ -30,7 +30,8 @@ def _declared():
 
 def test_header_declares_the_four_calls():
     names = _declared()
-    for n in ("dsa_indexer", "dsa_topk", "dsa_sparse_attn", "dsa_decode", "dsa_workspace_size", "dsa_last_error"):
+    for n in ("dsa_indexer", "dsa_topk", "dsa_sparse_attn", "dsa_decode", "dsa_prefill", "dsa_workspace_size",
+              "dsa_last_error"):
         assert n in names
 
 
@@ -138,6 +139,31 @@ def test_stage_events_validation(lib):
     assert lib.dsa_set_stage_events(ev, 3) == _lib.DSA_ERR_SHAPE
     assert lib.dsa_set_stage_events(ev, 4) == _lib.DSA_ERR_NULL
     assert lib.dsa_set_stage_events(None, 0) == _lib.DSA_OK
+
+
+def test_prefill_validation(lib):
+    kidx, kv = _cache(128, seq=4096), _cache(1152, seq=4096)
+
+    def f(b, ws=None, n=0, k=2048):
+        return lib.dsa_prefill(ctypes.byref(b), FAKE, None, FAKE, ctypes.byref(kidx), None, 64, 128, k, FAKE,
+                               ctypes.byref(kv), None, 128, 576, 512, 0.04, FAKE, None, None, ws, n, None)
+    assert f(_batch()) == _lib.DSA_ERR_SHAPE                   # q_start NULL: a decode batch
+    b = _batch(num_seqs=1, num_rows=3000, max_q=3000, max_len=3000, q_start=FAKE)
+    need = lib.dsa_workspace_size(_lib.DSA_WS_PREFILL, ctypes.byref(b), 2048, 128, 512)
+    assert need >= 3000 * 3000 * 4                              # the score matrix lives in the workspace
+    assert f(b) == _lib.DSA_ERR_WORKSPACE
+    assert f(b, FAKE, need - 1) == _lib.DSA_ERR_WORKSPACE
+    assert lib.dsa_workspace_size(_lib.DSA_WS_PREFILL, ctypes.byref(_batch()), 2048, 128, 512) == ctypes.c_size_t(-1).value
+    assert lib.dsa_workspace_size(_lib.DSA_WS_DECODE, ctypes.byref(b), 2048, 128, 512) == ctypes.c_size_t(-1).value
+
+
+def test_short_context_workspace_has_no_scores(lib):
+    """max_len <= k: no scores are computed, so the fused workspace holds no score matrix."""
+    short = _batch(num_seqs=1, num_rows=2000, max_q=2000, max_len=2000, q_start=FAKE)
+    long_ = _batch(num_seqs=1, num_rows=2000, max_q=2000, max_len=2049, q_start=FAKE)
+    ws_s = lib.dsa_workspace_size(_lib.DSA_WS_PREFILL, ctypes.byref(short), 2048, 128, 512)
+    ws_l = lib.dsa_workspace_size(_lib.DSA_WS_PREFILL, ctypes.byref(long_), 2048, 128, 512)
+    assert ws_s < 2000 * 2000 * 4 <= ws_l
 
 
 def test_workspace_sizes(lib):

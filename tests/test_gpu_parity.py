@@ -215,6 +215,49 @@ def test_fused_decode_matches_staged_bitwise(wl):
     assert torch.equal(lse_g, lse_f)
 
 
+# ------------------------------------------------------------------ fused prefill
+
+@pytest.mark.parametrize("wl", [W.TINY_PREFILL, W.SMALL_PREFILL, W.SMALL_CHUNKED], ids=lambda w: w.name)
+def test_fused_prefill_matches_staged_bitwise(wl):
+    announce("fused prefill vs staged", wl.name)
+    inp = W.generate(wl, DEV, chunk_index=1) if wl.chunk else W.generate(wl, DEV)
+    scores, idx_s, out_s, lse_s = gpu_staged(inp)
+    batch = dsa.Batch.from_inputs(inp)
+    idx_f = torch.empty_like(idx_s)
+    out_f, lse_f, _ = dsa.prefill(batch, inp.q8, inp.q_scale, inp.w, inp.k8, inp.k_scale, wl.k, inp.q, inp.kv,
+                                  inp.v, wl.scale, idx_out=idx_f, D_v=wl.D_v)
+    torch.cuda.synchronize()
+    assert torch.equal(idx_f, idx_s)
+    assert torch.equal(out_f.view(torch.int16), out_s.view(torch.int16))
+    assert torch.equal(lse_f, lse_s)
+
+
+@pytest.mark.parametrize("wl", [W.DENSE_PREFILL, W.DENSE_DECODE], ids=lambda w: w.name)
+def test_short_context_is_dense_attention(wl):
+    """max_len <= k: the fused entry points skip the indexer; the result is
+    dense causal attention over every prior token (checked against the oracle,
+    whose selection keeps every token when k >= t + 1)."""
+    announce("short-context dense path", wl.name)
+    inp = W.generate(wl, DEV)
+    batch = dsa.Batch.from_inputs(inp)
+    idx = torch.empty((inp.num_rows, wl.k), dtype=torch.int32, device=DEV)
+    call = dsa.prefill if inp.q_start is not None else dsa.decode
+    out, lse, _ = call(batch, inp.q8, inp.q_scale, inp.w, inp.k8, inp.k_scale, wl.k, inp.q, inp.kv, inp.v,
+                       wl.scale, idx_out=idx, D_v=wl.D_v)
+    torch.cuda.synchronize()
+    _, pos = inp.row_positions()
+    g_idx = to_np(idx)
+    for r, p in enumerate(pos):
+        assert g_idx[r][: p + 1].tolist() == list(range(p + 1))
+        assert (g_idx[r][p + 1:] == -1).all()
+    rows = list(range(inp.num_rows)) if inp.num_rows <= 64 else W.sample_rows(wl, inp.num_rows, 64, always=(0, inp.num_rows - 1))
+    a = arrays_of(inp)
+    ref = oracle.run_rows(a, rows)
+    g_out, g_lse = to_np(out), to_np(lse)
+    for i, r in enumerate(rows):
+        check_attention(g_out[r], g_lse[r], ref["out"][i], ref["lse"][i], f"{wl.name} row {r}")
+
+
 def test_binding_reports_bad_arguments():
     wl = W.SMALL_DECODE
     announce("binding error path")

@@ -2,7 +2,7 @@
 
 Holds shapes, seeds and random draws only; no part of the method is computed here.
 """
-from .configs import (ALL, BY_NAME, CHUNKED_128K, DECODE_128K, PAGED_DECODE_MIXED,  # noqa: F401
-                      PREFILL_32K, SMALL_CHUNKED, SMALL_DECODE, SMALL_PAGED, SMALL_PREFILL,
-                      TINY_PREFILL, Workload)
+from .configs import (ALL, BY_NAME, CHUNKED_128K, DECODE_128K, DENSE_DECODE, DENSE_PREFILL,  # noqa: F401
+                      PAGED_DECODE_MIXED, PREFILL_32K, SMALL_CHUNKED, SMALL_DECODE, SMALL_PAGED,
+                      SMALL_PREFILL, TINY_PREFILL, Workload)
 from .gen import Inputs, cache_of, generate, quantize_e4m3fn, sample_rows, synthetic_scores  # noqa: F401

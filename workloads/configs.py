@@ -80,3 +80,8 @@ SMALL_PAGED = PAGED_DECODE_MIXED.replace(
 SMALL_PREFILL = PREFILL_32K.replace(name="prefill_L2500", seq_len=2500, seed=12, sample_rows=0)
 SMALL_CHUNKED = CHUNKED_128K.replace(
     name="chunked_prefill_L3000_c1000", seq_len=3000, chunk=1000, seed=13, sample_rows=0)
+
+# Short contexts (every row sees at most k tokens): the selection is every
+# prior token and the fused entry points skip the indexer.
+DENSE_PREFILL = PREFILL_32K.replace(name="prefill_L1500_dense", seq_len=1500, seed=15, sample_rows=0)
+DENSE_DECODE = DECODE_128K.replace(name="decode_b4_ctx2048_dense", seqs=4, seq_len=2048, seed=16)
