@@ -72,6 +72,43 @@ def test_small_end_to_end(wl):
     assert same >= 0.9 * len(rows), f"only {same}/{len(rows)} rows selected the same set"
 
 
+# Budget and head-shape variants: other k, other indexer head counts, the
+# d_I = 32 indexer layout at production attention shapes, through the fused
+# entry points.
+VARIANTS = [
+    W.SMALL_DECODE.replace(name="decode_b3_ctx5000_k512_hi32", k=512, H_I=32, seed=21),
+    W.SMALL_DECODE.replace(name="decode_b3_ctx5000_k1024_hi48", k=1024, H_I=48, seed=22),
+    W.SMALL_DECODE.replace(name="decode_b3_ctx5000_k4096_hi16_di32", k=4096, H_I=16, d_I=32, seed=23),
+    W.SMALL_PAGED.replace(name="paged_decode_b5_mixed100_6000_k1024", k=1024, seed=24),
+    W.SMALL_PREFILL.replace(name="prefill_L2500_k512_hi8", k=512, H_I=8, seed=25),
+]
+
+
+@pytest.mark.parametrize("wl", VARIANTS, ids=[w.name for w in VARIANTS])
+def test_budget_and_shape_variants(wl):
+    announce("variant", wl.name)
+    inp = W.generate(wl, DEV)
+    batch = dsa.Batch.from_inputs(inp)
+    idx = torch.empty((inp.num_rows, wl.k), dtype=torch.int32, device=DEV)
+    call = dsa.prefill if inp.q_start is not None else dsa.decode
+    out, lse, _ = call(batch, inp.q8, inp.q_scale, inp.w, inp.k8, inp.k_scale, wl.k, inp.q, inp.kv, inp.v,
+                       wl.scale, idx_out=idx, D_v=wl.D_v)
+    scores = dsa.indexer(batch, inp.q8, inp.q_scale, inp.w, inp.k8, inp.k_scale)
+    torch.cuda.synchronize()
+    idx, out, lse, scores = to_np(idx), to_np(out), to_np(lse), to_np(scores)
+    a = arrays_of(inp)
+    rows = list(range(inp.num_rows)) if wl.kind == "decode" else W.sample_rows(
+        wl, inp.num_rows, 96, always=(0, wl.k - 1, wl.k, inp.num_rows - 1))
+    ref = oracle.run_rows(a, rows)
+    check_scores(scores, ref["scores"], oracle_abs_terms(a, rows), rows)
+    same = 0
+    for i, r in enumerate(rows):
+        if check_topk_swaps(idx[r], ref["idx"][i], ref["scores"][i], wl.k):
+            same += 1
+            check_attention(out[r], lse[r], ref["out"][i], ref["lse"][i], f"{wl.name} row {r}")
+    assert same >= 0.9 * len(rows), f"only {same}/{len(rows)} rows selected the same set"
+
+
 def test_small_chunked_prefill():
     wl = W.SMALL_CHUNKED
     first = W.generate(wl, DEV, chunk_index=0)
