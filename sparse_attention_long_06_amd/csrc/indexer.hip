@@ -106,6 +106,19 @@ __device__ __forceinline__ v4f mfma_dot(const Wide<DI>& a, const Wide<DI>& b) {
   return acc;
 }
 
+// ReLU of a finite MFMA result as a clamp to [0, FLT_MAX]: one v_med3_f32,
+// where fmaxf would add a NaN-quieting canonicalize.
+__device__ __forceinline__ float relu(float x) { return __builtin_amdgcn_fmed3f(x, 0.0f, 3.402823466e38f); }
+
+// Sum over the four 16-lane groups (rows) of a wave: after the row swaps every
+// lane holds the total of its column.  Pure VALU (no LDS permute).
+__device__ __forceinline__ float group_sum(float part) {
+  const auto r16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(part), __float_as_uint(part), false, false);
+  part = __uint_as_float(r16[0]) + __uint_as_float(r16[1]);
+  const auto r32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(part), __float_as_uint(part), false, false);
+  return __uint_as_float(r32[0]) + __uint_as_float(r32[1]);
+}
+
 template <int HT, int DI, int R, int RW, bool HIST>
 __global__ void __launch_bounds__(256) indexer_kernel(IndexerArgs a) {
   constexpr int KW = 4 / RW;            // waves sharing one row group (they split the keys)
@@ -204,13 +217,10 @@ __global__ void __launch_bounds__(256) indexer_kernel(IndexerArgs a) {
 #pragma unroll
             for (int ht = 0; ht < HT; ++ht) {
               const v4f acc = mfma_dot<DI>(qa[r][ht], kb);
-              part = fmaf(wq[r][ht][0], fmaxf(acc[0], 0.0f), part);
-              part = fmaf(wq[r][ht][1], fmaxf(acc[1], 0.0f), part);
-              part = fmaf(wq[r][ht][2], fmaxf(acc[2], 0.0f), part);
-              part = fmaf(wq[r][ht][3], fmaxf(acc[3], 0.0f), part);
+#pragma unroll
+              for (int i = 0; i < 4; ++i) part = fmaf(wq[r][ht][i], relu(acc[i]), part);
             }
-            part += __shfl_xor(part, 16);
-            part += __shfl_xor(part, 32);
+            part = group_sum(part);
             const int s = s0 + nl;
             if (grp == 0 && s < nrow[r]) {
               const float sc = part * ks[u];
@@ -445,19 +455,10 @@ __global__ void __launch_bounds__(256) indexer_decode_ring_kernel(IndexerArgs a)
 #pragma unroll
     for (int ht = 0; ht < HT; ++ht) {
       const v4f acc = mfma_dot<DI>(qa[ht], kb);
-      // ReLU as a clamp to [0, FLT_MAX]: the dot products are finite
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        part = fmaf(wq[ht][i], __builtin_amdgcn_fmed3f(acc[i], 0.0f, 3.402823466e38f), part);
+      for (int i = 0; i < 4; ++i) part = fmaf(wq[ht][i], relu(acc[i]), part);
     }
-    // sum over the four lane groups (rows of 16 lanes) holding key nl:
-    // the row swaps give every lane its neighbours' partial sums
-    {
-      const auto r16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(part), __float_as_uint(part), false, false);
-      part = __uint_as_float(r16[0]) + __uint_as_float(r16[1]);
-      const auto r32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(part), __float_as_uint(part), false, false);
-      part = __uint_as_float(r32[0]) + __uint_as_float(r32[1]);
-    }
+    part = group_sum(part);                   // the four lane groups holding key nl
     const int s = kbeg + ((wave + 4 * m) << 4) + nl;
     if (grp == 0 && s < kend) {
       const float sc = part * ks;
