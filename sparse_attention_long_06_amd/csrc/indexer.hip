@@ -477,6 +477,192 @@ __global__ void __launch_bounds__(256) indexer_decode_ring_kernel(IndexerArgs a)
   }
 }
 
+// ---------------------------------------------------------------------------
+// Prefill indexer with a workgroup-shared LDS ring (d_I = 128).
+//
+// A workgroup owns 8 consecutive query rows of one sequence (2 per wave) and
+// one chunk of keys.  Keys move through a ring of kPreRing slots of 64 keys,
+// filled by DMA that all four waves share (each wave moves a quarter of every
+// slot), so each key byte crosses from L2 once per workgroup and feeds 8 rows
+// x H_I heads of MFMAs.  One barrier per slot publishes it and retires the
+// slot the next DMA overwrites.  Rows compute every key of a full slot, also
+// keys past their own position (those entries of the score matrix are
+// unspecified), so every wave stores the same number of scores per slot and
+// the vector-memory counter the ring waits on stays exact.
+constexpr int kPreRing = 6;
+constexpr int kPreKeys = 64;
+
+template <int HT, bool SCALE>
+__global__ void __launch_bounds__(256) indexer_prefill_ring_kernel(IndexerArgs a) {
+  constexpr int DI = 128;
+  constexpr int R = 2;                                // rows per wave
+  constexpr int SLOT = kPreKeys * DI + kPreKeys * 4;  // keys + scales
+  constexpr int PER = SCALE ? 3 : 2;                  // DMA instructions per wave per slot
+  constexpr int ST = R * (kPreKeys / 16);             // score stores per wave per slot
+  __shared__ __attribute__((aligned(16))) char ring[kPreRing][SLOT];
+
+  const int b = blockIdx.z;
+  const int ytile = blockIdx.x % a.ntiles;
+  const int chunk_id = blockIdx.x / a.ntiles;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int nl = lane & 15, grp = lane >> 4;
+
+  const int len = a.g.seq_lens[b];
+  const int row0 = a.g.q_start[b];
+  const int nq = a.g.q_start[b + 1] - row0;
+  const int tile_r0 = ytile * 4 * R;
+  if (tile_r0 >= nq) return;
+  const int base_pos = len - nq;
+  const int last_r = min(tile_r0 + 4 * R, nq) - 1;
+  const int kbeg = chunk_id * a.chunk;
+  const int kend = min(kbeg + a.chunk, base_pos + last_r + 1);
+  if (kbeg >= kend) return;                           // uniform over the workgroup
+  const int nslots = (kend - kbeg + kPreKeys - 1) / kPreKeys;
+  // a partial row tile stores fewer scores per slot: it waits for everything
+  const bool exact = tile_r0 + 4 * R <= nq;
+
+  const uint32_t ring_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)&ring[0][0];
+  const bool off32 = a.kidx.row_stride < (1 << 26) && (!SCALE || a.ksc.row_stride < (1 << 26));
+  // lane offsets of this wave's two DMA instructions (slot keys 8i .. 8i+7,
+  // i = 2*wave + {0, 1}): key 8i + (lane >> 3), chunk (lane & 7) ^ swizzle;
+  // the swizzle of key n depends on n & 7 = lane >> 3 and on n >> 3 & 1 = i & 1
+  const int kn = lane >> 3, pc = lane & 7;
+  const uint32_t koff[2] = {(uint32_t)(kn * a.kidx.row_stride) + 16u * (uint32_t)(pc ^ kswz(kn)),
+                            (uint32_t)(kn * a.kidx.row_stride) + 16u * (uint32_t)(pc ^ kswz(8 + kn))};
+  const uint32_t soff = SCALE ? (uint32_t)(min(lane, 15) * a.ksc.row_stride) : 0u;
+
+  // first token row of 8 keys starting at s0 (8 keys never straddle a page)
+  auto row_of = [&](int s0) -> int64_t {
+    const int su = __builtin_amdgcn_readfirstlane(s0);
+    if (a.g.block_table) {
+      const auto* tbl = (const __attribute__((address_space(4))) int32_t*)(uintptr_t)a.g.block_table;
+      const int blk = tbl[(int64_t)b * a.g.max_blocks + (su >> a.g.block_shift)];
+      return ((int64_t)blk << a.g.block_shift) + (su & ((1 << a.g.block_shift) - 1));
+    }
+    return (int64_t)b * a.kidx.seq_stride + su;
+  };
+
+  auto issue = [&](int m) {
+    const uint32_t slot = ring_lds + (uint32_t)((m % kPreRing) * SLOT);
+    const int sbase = kbeg + m * kPreKeys;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int i = 2 * wave + h;                     // 8-key group of the slot
+      const int s0 = sbase + 8 * i;
+      const int last = kend - 1 - s0;                 // keys past the end re-read the last key
+      if (last >= 7 && off32) {
+        const char* kb = a.kidx.data + row_of(s0) * a.kidx.row_stride;
+        asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+                     :: "s"(slot + i * 1024u), "v"(koff[h]), "s"(kb) : "memory");
+      } else {
+        // ragged group: keys past kend re-read key kend-1; a group wholly past
+        // kend (last < 0) may start beyond the sequence, so it never looks up
+        // its own page and takes the page of key kend-1 instead
+        const int64_t r = last >= 0 ? row_of(s0) + min(kn, last) : token_row(a.g, a.kidx, b, kend - 1);
+        const char* src = a.kidx.data + r * a.kidx.row_stride + 16 * (pc ^ kswz(8 * (i & 1) + kn));
+        asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+                     :: "s"(slot + i * 1024u), "v"(src) : "memory");
+      }
+    }
+    if constexpr (SCALE) {
+      const int s0 = sbase + 16 * wave;              // this wave's 16 scales
+      const int last = kend - 1 - s0;
+      const uint32_t dst = slot + (uint32_t)(kPreKeys * DI + 64 * wave);
+      if (last >= 15 && off32 && !a.g.block_table) {
+        const char* sb = a.ksc.data + ((int64_t)b * a.ksc.seq_stride + s0) * a.ksc.row_stride;
+        if (lane < 16)
+          asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, %2"
+                       :: "s"(dst), "v"(soff), "s"(sb) : "memory");
+      } else {
+        const int key = s0 + min(lane, max(last, 0));
+        const char* src = a.ksc.data + token_row(a.g, a.ksc, b, min(key, kend - 1)) * a.ksc.row_stride;
+        if (lane < 16)
+          asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off"
+                       :: "s"(dst), "v"(src) : "memory");
+      }
+    }
+  };
+
+  // ring prologue first, then this wave's query rows (their loads overlap the
+  // prologue; the compiler waits for both before the rows are used)
+  for (int m = 0; m < kPreRing - 1 && m < nslots; ++m) issue(m);
+
+  Wide<DI> qa[R][HT];
+  float wq[R][HT][4];
+  int64_t trow[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int ri = tile_r0 + wave * R + r;
+    const bool ok = ri < nq;
+    const int t = row0 + (ok ? ri : 0);
+    trow[r] = ok ? t : -1;
+    const float qs = a.q_scale ? a.q_scale[t] : 1.0f;
+#pragma unroll
+    for (int ht = 0; ht < HT; ++ht) {
+      const int h = ht * 16 + nl;
+      Frag<DI> raw;
+      if (h < a.H_I)
+        load_frag<DI, false>(raw, reinterpret_cast<const char*>(a.q8) + ((int64_t)t * a.H_I + h) * DI, grp);
+      else
+        zero_frag<DI>(raw);
+      qa[r][ht] = widen<DI>(raw);
+      const int hw = ht * 16 + grp * 4;
+      const float4 w4 = hw < a.H_I ? *reinterpret_cast<const float4*>(a.w + (int64_t)t * a.H_I + hw)
+                                   : make_float4(0.f, 0.f, 0.f, 0.f);
+      wq[r][ht][0] = w4.x * qs;
+      wq[r][ht][1] = w4.y * qs;
+      wq[r][ht][2] = w4.z * qs;
+      wq[r][ht][3] = w4.w * qs;
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0x0F70);                 // rows and ring prologue are in
+
+  const int rb0 = nl * DI + 16 * ((2 * grp) ^ kswz(nl));
+  const int rb1 = nl * DI + 16 * ((2 * grp + 1) ^ kswz(nl));
+  for (int m = 0; m < nslots; ++m) {
+    const bool more = m + kPreRing - 1 < nslots;
+    if (more && exact) {
+      // Ops after this wave's slot-m DMA: the DMA of the next kPreRing-2
+      // slots and, once the ring is full, the stores of kPreRing-1 slots.
+      if (m >= kPreRing - 1)
+        wait_vmcnt<(kPreRing - 2) * PER + (kPreRing - 1) * ST>();
+      else
+        wait_vmcnt<(kPreRing - 2) * PER>();
+    } else {
+      wait_vmcnt<0>();
+    }
+    // every wave's part of slot m is in; every wave is done with slot m-1
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+    if (more) issue(m + kPreRing - 1);
+
+    const char* slot = &ring[m % kPreRing][0];
+#pragma unroll
+    for (int j = 0; j < kPreKeys / 16; ++j) {
+      Frag<DI> kf;
+      kf.lo = *reinterpret_cast<const v4i*>(slot + j * 16 * DI + rb0);
+      kf.hi = *reinterpret_cast<const v4i*>(slot + j * 16 * DI + rb1);
+      const float ks = SCALE ? *reinterpret_cast<const float*>(slot + kPreKeys * DI + 4 * (16 * j + nl)) : 1.0f;
+      const Wide<DI> kb = widen<DI>(kf);
+      const int s = kbeg + m * kPreKeys + 16 * j + nl;
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        float part = 0.0f;
+#pragma unroll
+        for (int ht = 0; ht < HT; ++ht) {
+          const v4f acc = mfma_dot<DI>(qa[r][ht], kb);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) part = fmaf(wq[r][ht][i], relu(acc[i]), part);
+        }
+        part = group_sum(part);
+        if (grp == 0 && s < kend && trow[r] >= 0) a.scores[trow[r] * a.ld + s] = part * ks;
+      }
+    }
+  }
+}
+
 template <int HT, int DI>
 static hipError_t launch_ht(const IndexerArgs& a, bool decode_layout, bool with_hist, hipStream_t s) {
   const dim3 grid(a.nchunks * a.ntiles, 1, a.g.num_seqs);
@@ -494,6 +680,9 @@ static hipError_t launch_ht(const IndexerArgs& a, bool decode_layout, bool with_
       hipLaunchKernelGGL((indexer_kernel<HT, DI, 1, 1, true>), grid, dim3(256), 0, s, a);
     else
       hipLaunchKernelGGL((indexer_kernel<HT, DI, 1, 1, false>), grid, dim3(256), 0, s, a);
+  } else if (DI == 128) {
+    if (a.ksc.data) hipLaunchKernelGGL((indexer_prefill_ring_kernel<HT, true>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((indexer_prefill_ring_kernel<HT, false>), grid, dim3(256), 0, s, a);
   } else {
     hipLaunchKernelGGL((indexer_kernel<HT, DI, kIdxRowsPerWave, 4, false>), grid, dim3(256), 0, s, a);
   }
