@@ -36,9 +36,9 @@ BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, vendor figure
 INDEXER_COUNTERS = {
     "sources": ["sparse_attention_long_06_amd/csrc/indexer.hip", "sparse_attention_long_06_amd/csrc/dsa_common.h",
                 "sparse_attention_long_06_amd/csrc/dsa_kernels.h", "sparse_attention_long_06_amd/csrc/api.hip"],
-    "sha256": "e1e28f1a1c638d33507bc68044dd17dcf7e69ccb0acb5c5cb2f3a05435b39bb1",
-    "fetch_kib": 272629.0,
-    "write_kib": 17231.2,
+    "sha256": "b5531726fe62866d03145b71569ed5ee126e0aafd9bcea09221c993ed1716794",
+    "fetch_kib": 272547.1,
+    "write_kib": 17231.1,
     "fetch_scale": 2.0,
     "write_scale": 1.0,
 }
