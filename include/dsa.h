@@ -192,12 +192,48 @@ dsa_status dsa_prefill(const dsa_batch* batch, const uint8_t* q8, const float* q
  */
 dsa_status dsa_set_stage_events(void* const* events, int count);
 
+/*
+ * dsa_indexer_warmup — the indexer's warm-up objective and its gradients
+ * (tenelement.pl article "DeepSeek V3.2-Exp Cuts Long-Context Costs with
+ * DeepSeek Sparse Attention (DSA) While Maintaining Benchmark Parity",
+ * section "Proces Treningu DSA: Od Warm-up do Sparsity": with the main model
+ * frozen, the indexer is fitted by a KL divergence to the dense attention
+ * distribution summed over the heads).  For query row t at position p:
+ *   target  a[s] = (1/H) sum_h softmax_s(scale * q[t,h] . K[s]),  s <= p
+ *   model   P[s] = softmax_s(I[t,s]),  I = the dsa_indexer score
+ *   loss[t] = sum_s a[s] (log a[s] - log P[s])
+ * and, for the pointers that are not NULL, the gradients of sum_t loss[t]
+ * with respect to the dequantised indexer query q_scale*q8 (dq), the head
+ * weights (dw) and the dequantised index keys k_scale*k8 (dk).  ReLU'(0) is
+ * taken as 0.  The dense side (q, kv) gets no gradient (it is frozen).
+ *   q, kv   as dsa_sparse_attn with D = 576 (K is the whole row; V is unused)
+ *   q8, q_scale, w, kidx, kscale   as dsa_indexer, d_I = 128, H_I in {32, 64}
+ *   loss    [T] fp32 out
+ *   dq      [T, H_I, 128] fp32 out, or NULL
+ *   dw      [T, H_I] fp32 out, or NULL
+ *   dk      [B, max_len, 128] fp32 out (token s of sequence b at row
+ *           b*max_len + s; tokens at or past seq_lens[b] get 0), or NULL;
+ *           16-byte aligned
+ *   workspace: dsa_workspace_size(DSA_WS_WARMUP, batch, 0, H, 0) bytes,
+ *           256-byte aligned
+ * Batch: q_start must be set (rows per sequence, as dsa_prefill) and the
+ * caches contiguous (block_table NULL), else DSA_ERR_SHAPE / DSA_ERR_UNSUPPORTED.
+ * Supported: D = 576, H a multiple of 16 in [16, 128].  Results are
+ * deterministic (fixed-order reductions, no float atomics).
+ */
+dsa_status dsa_indexer_warmup(const dsa_batch* batch, const uint16_t* q, const dsa_cache* kv, int H, int D,
+                              float scale, const uint8_t* q8, const float* q_scale, const float* w,
+                              const dsa_cache* kidx, const dsa_cache* kscale, int H_I, int d_I,
+                              float* loss, float* dq, float* dw, float* dk,
+                              void* workspace, size_t ws_bytes, void* stream);
+
 /* Which call dsa_workspace_size() sizes. */
-enum { DSA_WS_TOPK = 1, DSA_WS_ATTN = 2, DSA_WS_DECODE = 3, DSA_WS_PREFILL = 4 };
+enum { DSA_WS_TOPK = 1, DSA_WS_ATTN = 2, DSA_WS_DECODE = 3, DSA_WS_PREFILL = 4, DSA_WS_WARMUP = 5 };
 
 /*
  * Workspace bytes `entry` needs for this batch (host-only; no device call).
- * H and D_v matter for DSA_WS_ATTN / DSA_WS_DECODE / DSA_WS_PREFILL only.  Returns 0 when the
+ * H and D_v matter for DSA_WS_ATTN / DSA_WS_DECODE / DSA_WS_PREFILL only;
+ * DSA_WS_WARMUP takes H (the dense heads) and ignores k and D_v.  Returns 0 when the
  * call needs none, and (size_t)-1 for invalid arguments.
  */
 size_t dsa_workspace_size(int entry, const dsa_batch* batch, int k, int H, int D_v);

@@ -10,6 +10,8 @@ Stages (see include/dsa.h for the full contract):
     topk(...)         per-row top-k token indices
     sparse_attn(...)  MQA attention over the selected tokens
     decode(...)       the three chained for one query per sequence
+    prefill(...)      the three chained for query rows per sequence
+    indexer_warmup(...)  the indexer's KL warm-up objective and its gradients
 """
 from __future__ import annotations
 
@@ -20,9 +22,11 @@ from typing import Optional
 import torch
 
 from . import _lib
-from ._lib import DSA_WS_ATTN, DSA_WS_DECODE, DSA_WS_PREFILL, DSA_WS_TOPK, DsaBatch, DsaCache  # noqa: F401
+from ._lib import (DSA_WS_ATTN, DSA_WS_DECODE, DSA_WS_PREFILL, DSA_WS_TOPK, DSA_WS_WARMUP,  # noqa: F401
+                   DsaBatch, DsaCache)
 
-__all__ = ["Batch", "DsaError", "indexer", "topk", "sparse_attn", "decode", "workspace_size", "cache_view"]
+__all__ = ["Batch", "DsaError", "indexer", "topk", "sparse_attn", "decode", "prefill", "indexer_warmup",
+           "workspace_size", "cache_view"]
 
 
 class DsaError(RuntimeError):
@@ -198,3 +202,37 @@ def prefill(batch: Batch, q8, q_scale, w, k8, k_scale, k: int, q, kv, v, scale: 
     """Whole path for query rows per sequence (dsa_prefill); returns (out, lse, idx_out)."""
     return _fused("dsa_prefill", DSA_WS_PREFILL, batch, q8, q_scale, w, k8, k_scale, k, q, kv, v, scale,
                   out, lse, idx_out, workspace, D_v)
+
+
+def indexer_warmup(batch: Batch, q, kv, scale: float, q8, q_scale, w, k8, k_scale, grads: bool = True,
+                   loss=None, dq=None, dw=None, dk=None, workspace=None):
+    """The indexer's warm-up objective (dsa_indexer_warmup).
+
+    Returns (loss [T], dq [T,H_I,d_I], dw [T,H_I], dk [B,max_len,d_I]); the
+    gradients are None when ``grads`` is False and no buffer is passed.
+    """
+    lib = _lib.load()
+    T, H, D = (int(x) for x in q.shape)
+    H_I, d_I = int(q8.shape[1]), int(q8.shape[2])
+    dev = q.device
+    if loss is None:
+        loss = torch.empty(T, dtype=torch.float32, device=dev)
+    if grads:
+        if dq is None:
+            dq = torch.empty((T, H_I, d_I), dtype=torch.float32, device=dev)
+        if dw is None:
+            dw = torch.empty((T, H_I), dtype=torch.float32, device=dev)
+        if dk is None:
+            dk = torch.empty((batch.num_seqs, batch.max_len, d_I), dtype=torch.float32, device=dev)
+    ws_n = workspace_size(DSA_WS_WARMUP, batch, 0, H, 0)
+    if workspace is None:
+        workspace = _workspace(ws_n, dev)
+    elif workspace.numel() < ws_n:
+        raise ValueError(f"workspace too small: {workspace.numel()} < {ws_n}")
+    b = batch.c()
+    kvc = cache_view(kv, batch)
+    kc, sc = cache_view(k8, batch), cache_view(k_scale, batch)
+    _check(lib.dsa_indexer_warmup(ctypes.byref(b), _ptr(q), _ref(kvc), H, D, float(scale), _ptr(q8), _ptr(q_scale),
+                                  _ptr(w), _ref(kc), _ref(sc), H_I, d_I, _ptr(loss), _ptr(dq), _ptr(dw), _ptr(dk),
+                                  _ptr(workspace), ws_n, _stream(dev)), "dsa_indexer_warmup")
+    return loss, dq, dw, dk

@@ -193,6 +193,31 @@ FusedPlan plan_fused(int T, int max_len, int k, int H, int D_v) {
   return p;
 }
 
+// Workspace of dsa_indexer_warmup: the [T, ld] score matrix (overwritten by
+// dI), the per-head dense log-sum-exps and the per-chunk key-gradient partials.
+struct WarmPlan {
+  int64_t ld = 0;
+  int row_chunk = 0, nchunk = 0;
+  size_t off_scores = 0, off_lse = 0, off_dk = 0, bytes = 0;
+};
+
+WarmPlan plan_warmup(int T, int B, int max_len, int max_q, int H) {
+  WarmPlan p;
+  p.ld = round_up(max_len, 4);
+  // at most 16 chunks of rows per key tile, at least 64 rows each
+  p.row_chunk = (int)round_up((max_q + 15) / 16, 4);
+  if (p.row_chunk < 64) p.row_chunk = 64;
+  p.nchunk = (max_q + p.row_chunk - 1) / p.row_chunk;
+  size_t o = 0;
+  p.off_scores = o; o += (size_t)T * p.ld * 4;
+  o = (size_t)round_up((int64_t)o, 256);
+  p.off_lse = o; o += (size_t)T * H * 4;
+  o = (size_t)round_up((int64_t)o, 256);
+  p.off_dk = o; o += (size_t)p.nchunk * B * max_len * 128 * 4;
+  p.bytes = (size_t)round_up((int64_t)o, 256);
+  return p;
+}
+
 // ---------------------------------------------------------------- launch sequences
 
 dsa_status run_indexer(const dsa_batch* b, const uint8_t* q8, const float* q_scale, const float* w,
@@ -348,7 +373,12 @@ extern "C" dsa_status dsa_set_stage_events(void* const* events, int count) {
 }
 
 extern "C" size_t dsa_workspace_size(int entry, const dsa_batch* batch, int k, int H, int D_v) {
-  if (check_batch(batch) != DSA_OK || k < 1 || k > 4096) return (size_t)-1;
+  if (check_batch(batch) != DSA_OK) return (size_t)-1;
+  if (entry == DSA_WS_WARMUP) {
+    if (H < 1 || !batch->q_start) return (size_t)-1;
+    return plan_warmup(batch->num_rows, batch->num_seqs, batch->max_len, batch->max_q, H).bytes;
+  }
+  if (k < 1 || k > 4096) return (size_t)-1;
   switch (entry) {
     case DSA_WS_TOPK:
       return plan_topk(batch->num_rows, batch->max_len, k).bytes;
@@ -511,4 +541,66 @@ extern "C" dsa_status dsa_prefill(const dsa_batch* batch, const uint8_t* q8, con
   st = run_fused(batch, q8, q_scale, w, kidx, kscale, H_I, d_I, k, q, kv, v, H, D, D_v, scale, out, lse, idx_out, p,
                  static_cast<char*>(workspace), static_cast<hipStream_t>(stream));
   return st == DSA_OK ? ok() : st;
+}
+
+extern "C" dsa_status dsa_indexer_warmup(const dsa_batch* batch, const uint16_t* q, const dsa_cache* kv, int H,
+                                         int D, float scale, const uint8_t* q8, const float* q_scale,
+                                         const float* w, const dsa_cache* kidx, const dsa_cache* kscale, int H_I,
+                                         int d_I, float* loss, float* dq, float* dw, float* dk, void* workspace,
+                                         size_t ws_bytes, void* stream) {
+  dsa_status st = check_batch(batch);
+  if (st != DSA_OK) return st;
+  CHECK(batch->q_start != nullptr, DSA_ERR_SHAPE, "dsa_indexer_warmup takes query rows per sequence (q_start must be set)");
+  CHECK(batch->block_table == nullptr, DSA_ERR_UNSUPPORTED, "dsa_indexer_warmup supports contiguous caches only");
+  st = check_indexer_args(batch, q8, w, kidx, kscale, H_I, d_I);
+  if (st != DSA_OK) return st;
+  CHECK(d_I == 128 && (H_I == 32 || H_I == 64), DSA_ERR_UNSUPPORTED,
+        "warm-up objective supports d_I = 128 with H_I in {32, 64} (got d_I %d, H_I %d)", d_I, H_I);
+  CHECK(q && loss, DSA_ERR_NULL, "q or loss is NULL");
+  CHECK(D == 576, DSA_ERR_UNSUPPORTED, "warm-up objective supports D = 576 (got %d)", D);
+  CHECK(H >= 16 && H <= 128 && H % 16 == 0, DSA_ERR_UNSUPPORTED, "H %d not a multiple of 16 in [16, 128]", H);
+  CHECK(isfinite(scale), DSA_ERR_SHAPE, "scale is not finite");
+  CHECK(aligned(q, 16), DSA_ERR_ALIGN, "q not 16-byte aligned");
+  CHECK(aligned(w, 16), DSA_ERR_ALIGN, "w not 16-byte aligned");
+  CHECK(!dk || aligned(dk, 16), DSA_ERR_ALIGN, "dk not 16-byte aligned");
+  st = check_cache(batch, kv, "kv", (int64_t)D * 2, 16);
+  if (st != DSA_OK) return st;
+  const WarmPlan p = plan_warmup(batch->num_rows, batch->num_seqs, batch->max_len, batch->max_q, H);
+  CHECK(workspace, DSA_ERR_WORKSPACE, "warm-up needs %zu workspace bytes, got NULL", p.bytes);
+  CHECK(ws_bytes >= p.bytes, DSA_ERR_WORKSPACE, "warm-up needs %zu workspace bytes, got %zu", p.bytes, ws_bytes);
+  CHECK(aligned(workspace, 256), DSA_ERR_ALIGN, "workspace not 256-byte aligned");
+  if (batch->num_rows == 0 && !dk) return ok();     // with dk set, the zero gradient is still written
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  float* scores = reinterpret_cast<float*>(ws + p.off_scores);
+  if (batch->num_rows > 0) {
+    st = run_indexer(batch, q8, q_scale, w, kidx, kscale, H_I, d_I, scores, p.ld, nullptr, s);
+    if (st != DSA_OK) return st;
+  }
+  WarmArgs a;
+  a.g = make_geo(batch);
+  a.kv = make_cache(kv);
+  a.q = q;
+  a.H = H;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.inv_H = 1.0f / (float)H;
+  a.lse2 = reinterpret_cast<float*>(ws + p.off_lse);
+  a.scores = scores;
+  a.ld = p.ld;
+  a.loss = loss;
+  a.kidx = make_cache(kidx);
+  a.ksc = make_cache((kscale && kscale->data) ? kscale : nullptr);
+  a.q8 = q8;
+  a.q_scale = q_scale;
+  a.w = w;
+  a.H_I = H_I;
+  a.dq = dq;
+  a.dw = dw;
+  a.dk_part = reinterpret_cast<float*>(ws + p.off_dk);
+  a.dk = dk;
+  a.max_len = batch->max_len;
+  a.row_chunk = p.row_chunk;
+  a.nchunk = p.nchunk;
+  LAUNCH(launch_warmup(a, s), "warm-up launch");
+  return ok();
 }

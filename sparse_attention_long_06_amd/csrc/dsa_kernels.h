@@ -90,4 +90,33 @@ struct CombineArgs {
 hipError_t launch_attn(const AttnArgs& a, int D, int D_v, hipStream_t stream);
 hipError_t launch_combine(const CombineArgs& a, hipStream_t stream);
 
+// ---------------------------------------------------------------- indexer warm-up objective
+struct WarmArgs {
+  Geo g;                 // contiguous caches, query rows per sequence
+  Cache kv;              // 576 bf16 per token (K = the whole latent row)
+  const uint16_t* q;     // [T, H, 576] bf16
+  int H;                 // a multiple of 16 in [16, 128]
+  float scale_log2;      // softmax scale * log2(e)
+  float inv_H;
+  float* lse2;           // [T, H] log2-sum-exp2 of the scaled dense logits
+  float* scores;         // [T, ld] indexer scores in, dI out (entries s <= p_t)
+  int64_t ld;
+  float* loss;           // [T]
+  Cache kidx;            // 128 FP8 bytes per token
+  Cache ksc;             // fp32 per token or data == nullptr (= 1)
+  const uint8_t* q8;     // [T, H_I, 128]
+  const float* q_scale;  // [T] or nullptr
+  const float* w;        // [T, H_I]
+  int H_I;               // 32 or 64
+  float* dq;             // [T, H_I, 128] or nullptr
+  float* dw;             // [T, H_I] or nullptr
+  float* dk_part;        // [nchunk, B, max_len, 128] per-chunk partials
+  float* dk;             // [B, max_len, 128] or nullptr
+  int max_len;
+  int row_chunk;         // query rows per dk chunk
+  int nchunk;
+};
+
+hipError_t launch_warmup(const WarmArgs& a, hipStream_t stream);
+
 }  // namespace dsa

@@ -30,7 +30,8 @@ def _declared():
 
 def test_header_declares_the_four_calls():
     names = _declared()
-    for n in ("dsa_indexer", "dsa_topk", "dsa_sparse_attn", "dsa_decode", "dsa_prefill", "dsa_workspace_size",
+    for n in ("dsa_indexer", "dsa_topk", "dsa_sparse_attn", "dsa_decode", "dsa_prefill", "dsa_indexer_warmup",
+              "dsa_workspace_size",
               "dsa_last_error"):
         assert n in names
 
@@ -183,3 +184,29 @@ def test_workspace_sizes(lib):
 def test_binding_fails_loudly_without_library(tmp_path):
     with pytest.raises(RuntimeError, match="missing"):
         _lib.load(str(tmp_path / "libdsa.so"))
+
+
+def test_warmup_validation(lib):
+    kidx, kv = _cache(128, seq=4096), _cache(1152, seq=4096)
+    pre = _batch(num_seqs=1, num_rows=3000, max_q=3000, max_len=3000, q_start=FAKE)
+
+    def f(b, ws=None, n=0, H=128, D=576, H_I=64, d_I=128, loss=FAKE, dk=None, kvc=kv):
+        return lib.dsa_indexer_warmup(ctypes.byref(b), FAKE, ctypes.byref(kvc), H, D, 0.04, FAKE, None, FAKE,
+                                      ctypes.byref(kidx), None, H_I, d_I, loss, None, None, dk, ws, n, None)
+    need = lib.dsa_workspace_size(_lib.DSA_WS_WARMUP, ctypes.byref(pre), 0, 128, 0)
+    assert need >= 3000 * 3000 * 4 + 3000 * 128 * 4            # scores/dI and the per-head log-sum-exps
+    assert f(_batch()) == _lib.DSA_ERR_SHAPE                     # decode batch: no q_start
+    assert f(_batch(num_seqs=1, num_rows=4, max_q=4, max_len=64, q_start=FAKE, block_table=FAKE,
+                    max_blocks=1, block_size=64)) == _lib.DSA_ERR_UNSUPPORTED   # paged caches
+    assert f(pre, FAKE, need, H_I=48) == _lib.DSA_ERR_UNSUPPORTED
+    assert f(pre, FAKE, need, d_I=32) == _lib.DSA_ERR_UNSUPPORTED
+    assert f(pre, FAKE, need, D=64) == _lib.DSA_ERR_UNSUPPORTED
+    assert f(pre, FAKE, need, H=72) == _lib.DSA_ERR_UNSUPPORTED
+    assert f(pre, FAKE, need, loss=None) == _lib.DSA_ERR_NULL
+    assert f(pre, FAKE, need, dk=FAKE + 4) == _lib.DSA_ERR_ALIGN
+    assert f(pre) == _lib.DSA_ERR_WORKSPACE
+    assert f(pre, FAKE, need - 1) == _lib.DSA_ERR_WORKSPACE
+    assert f(pre, FAKE, need, kvc=_cache(1152, seq=100)) == _lib.DSA_ERR_SHAPE      # kv seq_stride < max_len
+    # the workspace size ignores k and needs q_start
+    assert lib.dsa_workspace_size(_lib.DSA_WS_WARMUP, ctypes.byref(pre), 99999, 128, 0) == need
+    assert lib.dsa_workspace_size(_lib.DSA_WS_WARMUP, ctypes.byref(_batch()), 0, 128, 0) == ctypes.c_size_t(-1).value

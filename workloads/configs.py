@@ -85,3 +85,12 @@ SMALL_CHUNKED = CHUNKED_128K.replace(
 # prior token and the fused entry points skip the indexer.
 DENSE_PREFILL = PREFILL_32K.replace(name="prefill_L1500_dense", seq_len=1500, seed=15, sample_rows=0)
 DENSE_DECODE = DECODE_128K.replace(name="decode_b4_ctx2048_dense", seqs=4, seq_len=2048, seed=16)
+
+# Indexer warm-up objective (KL of the head-averaged dense attention against the
+# indexer softmax, forward and backward): every token of one sequence is a
+# query row, as in training.
+WARMUP_4K = PREFILL_32K.replace(name="warmup_L4k", seq_len=4096, seed=17, sample_rows=32)
+SMALL_WARMUP = PREFILL_32K.replace(name="warmup_L300", seq_len=300, seed=18, sample_rows=0)
+INT_WARMUP = PREFILL_32K.replace(name="warmup_L200_int", seq_len=200, seed=19, sample_rows=0,
+                                 integer_indexer=True)
+RAGGED_WARMUP = PREFILL_32K.replace(name="warmup_b2_L260", seqs=2, seq_len=260, seed=20, sample_rows=0)
