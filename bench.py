@@ -383,6 +383,136 @@ def run_chunked(args, wl):
     }
 
 
+def run_warmup(args):
+    """One step = the indexer warm-up objective with all three gradients
+    (dsa_indexer_warmup) over every token of the sequence as a query row."""
+    import torch
+
+    import workloads as W
+    import sparse_attention_long_06_amd as dsa
+    from sparse_attention_long_06_amd import _lib
+
+    wl = W.BY_NAME[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    print(f"[bench] generating {wl.name} on {dev}", file=sys.stderr, flush=True)
+    inp = W.generate(wl, dev)
+    batch = dsa.Batch.from_inputs(inp)
+    T = inp.num_rows
+    loss = torch.empty(T, dtype=torch.float32, device=dev)
+    dq = torch.empty((T, wl.H_I, wl.d_I), dtype=torch.float32, device=dev)
+    dw = torch.empty((T, wl.H_I), dtype=torch.float32, device=dev)
+    dk = torch.empty((batch.num_seqs, batch.max_len, wl.d_I), dtype=torch.float32, device=dev)
+    ws = torch.empty(dsa.workspace_size(dsa.DSA_WS_WARMUP, batch, 0, wl.H, 0), dtype=torch.uint8, device=dev)
+
+    def step():
+        dsa.indexer_warmup(batch, inp.q, inp.kv, wl.scale, inp.q8, inp.q_scale, inp.w, inp.k8, inp.k_scale,
+                           loss=loss, dq=dq, dw=dw, dk=dk, workspace=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    print(f"[bench] timing {args.steps} warm-up objective steps", file=sys.stderr, flush=True)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    for _ in range(args.steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms = e0.elapsed_time(e1) / args.steps
+
+    # instrumented pass: HIP events recorded by the library between its stages
+    hip = _hip()
+    names = ["indexer", "dense_lse", "target_kl", "dq_dw", "dk"]
+    evs = [ctypes.c_void_p() for _ in range(6)]
+    for e in evs:
+        hip.hipEventCreate(ctypes.byref(e))
+    arr = (ctypes.c_void_p * 6)(*[e.value for e in evs])
+    lib = _lib.load()
+    acc = [0.0] * 5
+    for _ in range(args.steps):
+        assert lib.dsa_set_stage_events(arr, 6) == 0
+        step()
+        torch.cuda.synchronize()
+        for i in range(5):
+            f = ctypes.c_float()
+            hip.hipEventElapsedTime(ctypes.byref(f), evs[i], evs[i + 1])
+            acc[i] += f.value
+    st = {n: a / args.steps for n, a in zip(names, acc)}
+    for e in evs:
+        hip.hipEventDestroy(e)
+
+    _, pos = inp.row_positions()
+    pairs = sum(p + 1 for p in pos)
+    flops = {"indexer": 2 * wl.H_I * wl.d_I * pairs,
+             "dense_lse": 2 * wl.H * wl.D * pairs,
+             "target_kl": 2 * wl.H * wl.D * pairs,
+             "dq_dw": 2 * 2 * wl.H_I * wl.d_I * pairs,      # z recomputed + the dq contraction
+             "dk": 2 * 2 * wl.H_I * wl.d_I * pairs}
+    tfs = {k: flops[k] / (st[k] * 1e-3) / 1e12 for k in names}
+    dom = max(names, key=lambda k: st[k])
+    kernel = {"indexer": "indexer_prefill_ring_kernel", "dense_lse": "warm_attn_kernel<0> (dense log-sum-exp pass)",
+              "target_kl": "warm_attn_kernel<1> (target, KL, dI)", "dq_dw": "warm_dq_kernel",
+              "dk": "warm_dk_kernel + warm_dk_reduce_kernel"}[dom]
+    res = {
+        "metric": f"DSA indexer warm-up objective tokens/s (KL forward + dq/dw/dk backward, L={wl.seq_len})",
+        "value": round(T / (ms * 1e-3), 1), "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 3),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp8-storage/bf16-mfma",
+        "data": "synthetic (seeded N(0,1) draws, per-token e4m3fn quantised indexer q/k; bf16 q and latent KV)",
+        "config": {"workload": wl.name, "rows": T, "context": wl.seq_len, "H_I": wl.H_I, "d_I": wl.d_I,
+                   "H": wl.H, "D": wl.D, "parallelism": "single GPU"},
+        "roofline": {"bound": "mfma", "kernel": kernel, "achieved": round(tfs[dom], 1),
+                     "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(tfs[dom] / BF16_PEAK_TFLOPS, 4),
+                     "traffic": None, "flops_per_launch": flops[dom], "launch_ms": round(st[dom], 4)},
+        "stages_ms": {k: round(v, 4) for k, v in st.items()},
+        "stages_tflops": {k: round(v, 1) for k, v in tfs.items()},
+        "wall_s": round(elapsed, 3),
+    }
+    if args.no_cpu_baseline:
+        res["cpu_baseline"] = None
+    else:
+        res["cpu_baseline"] = cpu_baseline_warmup(inp, args.cpu_budget)
+    return res
+
+
+def cpu_baseline_warmup(inp, budget_s: float):
+    """The warm-up oracle on whole rows, longest first, until ~budget_s of work is done."""
+    from oracle import warmup_oracle
+    from tests.oracle_io import arrays_of
+
+    a = arrays_of(inp.to("cpu"))
+    threads = _oracle_threads()
+    T = inp.num_rows
+    done = 0
+    t0 = time.perf_counter()
+    while True:
+        warmup_oracle.run_warmup(a, [T - 1 - (done % T)])
+        done += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    el = time.perf_counter() - t0
+    rows = [T - 1 - (i % T) for i in range(done)]
+    # the per-row cost grows with the row's position: scale the sampled rate to the whole sequence
+    sampled_pairs = sum(r + 1 for r in rows)
+    all_pairs = T * (T + 1) // 2
+    rate = T / (el * all_pairs / sampled_pairs)
+    return {"value": round(rate, 4), "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{done} query rows of {inp.wl.name} from the last backwards (loss, dq, dw, dk of each, "
+                      f"{sampled_pairs} causal pairs in {el:.1f} s), fp64 NumPy; rate scaled to all "
+                      f"{all_pairs} pairs of the sequence"}
+
+
+def _oracle_threads():
+    try:
+        import threadpoolctl
+        return max(i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()) or os.cpu_count()
+    except Exception:  # noqa: BLE001
+        return os.cpu_count()
+
+
 def cpu_baseline(inp, budget_s: float):
     """Time the CPU oracle on whole decode queries until ~budget_s of work is done."""
     import oracle
@@ -440,6 +570,9 @@ def main():
         copy_calibration(args.copy_calibration)
         return
     import workloads as W
+    if args.workload.startswith("warmup"):
+        print(json.dumps(run_warmup(args)), flush=True)
+        return
     if W.BY_NAME[args.workload].kind in ("prefill", "chunked_prefill"):
         print(json.dumps(run_prefill(args)), flush=True)
         return

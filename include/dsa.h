@@ -178,17 +178,22 @@ dsa_status dsa_prefill(const dsa_batch* batch, const uint8_t* q8, const float* q
                        void* workspace, size_t ws_bytes, void* stream);
 
 /*
- * dsa_set_stage_events — opt-in stage timing for the NEXT dsa_decode or
- * dsa_prefill call on
- * this thread (for profiling tools; the stages are the ones the pages name:
- * indexer, selection, core attention).  `events` holds `count` >= 4 hipEvent_t
- * handles created by the caller; that call records them on its stream:
- *   events[0] before the indexer (after the workspace clear),
- *   events[1] after the indexer, events[2] after the top-k,
- *   events[3] after the attention (and its split combine).
+ * dsa_set_stage_events — opt-in stage timing for the NEXT dsa_decode,
+ * dsa_prefill or dsa_indexer_warmup call on this thread (for profiling
+ * tools; the stages are the ones the pages name: indexer, selection, core
+ * attention).  `events` holds `count` >= 4 hipEvent_t handles created by the
+ * caller (at most 6 are used); that call records them on its stream:
+ *   dsa_decode / dsa_prefill (4 events):
+ *     events[0] before the indexer (after the workspace clear),
+ *     events[1] after the indexer, events[2] after the top-k,
+ *     events[3] after the attention (and its split combine);
+ *   dsa_indexer_warmup (the first min(count, 6)):
+ *     events[0] before the indexer, events[1] after it, events[2] after the
+ *     dense log-sum-exp pass, events[3] after the target/KL pass,
+ *     events[4] after dq/dw, events[5] after dk.
  * The registration is consumed by that one call.  NULL clears it.
- * Errors: DSA_ERR_SHAPE if count < 4.  A failed record returns DSA_ERR_HIP
- * from dsa_decode.
+ * Errors: DSA_ERR_SHAPE if count < 4, DSA_ERR_NULL if one of the first
+ * min(count, 6) is NULL.  A failed record returns DSA_ERR_HIP from the call.
  */
 dsa_status dsa_set_stage_events(void* const* events, int count);
 

@@ -15,7 +15,9 @@ using namespace dsa;
 namespace {
 
 thread_local std::string g_err;
-thread_local hipEvent_t g_stage_events[4] = {nullptr, nullptr, nullptr, nullptr};
+constexpr int kMaxStageEvents = 6;
+thread_local hipEvent_t g_stage_events[kMaxStageEvents] = {};
+thread_local int g_stage_count = 0;
 thread_local bool g_stage_armed = false;
 
 dsa_status fail(dsa_status s, const char* fmt, ...) {
@@ -363,11 +365,11 @@ extern "C" dsa_status dsa_set_stage_events(void* const* events, int count) {
     g_stage_armed = false;
     return ok();
   }
-  CHECK(count >= 4, DSA_ERR_SHAPE, "need 4 stage events, got %d", count);
-  for (int i = 0; i < 4; ++i) {
-    CHECK(events[i], DSA_ERR_NULL, "stage event %d is NULL", i);
-    g_stage_events[i] = static_cast<hipEvent_t>(events[i]);
-  }
+  CHECK(count >= 4, DSA_ERR_SHAPE, "need at least 4 stage events, got %d", count);
+  const int n = count < kMaxStageEvents ? count : kMaxStageEvents;
+  for (int i = 0; i < n; ++i) CHECK(events[i], DSA_ERR_NULL, "stage event %d is NULL", i);
+  for (int i = 0; i < n; ++i) g_stage_events[i] = static_cast<hipEvent_t>(events[i]);
+  g_stage_count = n;
   g_stage_armed = true;
   return ok();
 }
@@ -571,12 +573,17 @@ extern "C" dsa_status dsa_indexer_warmup(const dsa_batch* batch, const uint16_t*
   CHECK(aligned(workspace, 256), DSA_ERR_ALIGN, "workspace not 256-byte aligned");
   if (batch->num_rows == 0 && !dk) return ok();     // with dk set, the zero gradient is still written
   hipStream_t s = static_cast<hipStream_t>(stream);
+  const int nmark = g_stage_armed ? g_stage_count : 0;
+  g_stage_armed = false;
+  auto mark = [&](int i) -> hipError_t { return i < nmark ? hipEventRecord(g_stage_events[i], s) : hipSuccess; };
   char* ws = static_cast<char*>(workspace);
   float* scores = reinterpret_cast<float*>(ws + p.off_scores);
+  LAUNCH(mark(0), "stage event");
   if (batch->num_rows > 0) {
     st = run_indexer(batch, q8, q_scale, w, kidx, kscale, H_I, d_I, scores, p.ld, nullptr, s);
     if (st != DSA_OK) return st;
   }
+  LAUNCH(mark(1), "stage event");
   WarmArgs a;
   a.g = make_geo(batch);
   a.kv = make_cache(kv);
@@ -601,6 +608,9 @@ extern "C" dsa_status dsa_indexer_warmup(const dsa_batch* batch, const uint16_t*
   a.max_len = batch->max_len;
   a.row_chunk = p.row_chunk;
   a.nchunk = p.nchunk;
-  LAUNCH(launch_warmup(a, s), "warm-up launch");
+  for (int stage = 0; stage < 4; ++stage) {
+    LAUNCH(launch_warmup(a, stage, s), "warm-up launch");
+    LAUNCH(mark(2 + stage), "stage event");
+  }
   return ok();
 }

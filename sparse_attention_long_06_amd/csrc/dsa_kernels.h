@@ -117,6 +117,7 @@ struct WarmArgs {
   int nchunk;
 };
 
-hipError_t launch_warmup(const WarmArgs& a, hipStream_t stream);
+// stage 0: dense log-sum-exp pass; 1: target, KL and dI; 2: dq and dw; 3: dk
+hipError_t launch_warmup(const WarmArgs& a, int stage, hipStream_t stream);
 
 }  // namespace dsa

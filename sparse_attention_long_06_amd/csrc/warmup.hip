@@ -589,20 +589,30 @@ __global__ void __launch_bounds__(256) warm_dk_reduce_kernel(WarmArgs a) {
 
 }  // namespace
 
-hipError_t launch_warmup(const WarmArgs& a, hipStream_t s) {
+hipError_t launch_warmup(const WarmArgs& a, int stage, hipStream_t s) {
   const int T = a.g.num_rows;
   const dim3 blk_attn(64 * (a.H / 16));
-  if (T > 0) {
-    hipLaunchKernelGGL(warm_attn_kernel<0>, dim3(T), blk_attn, 0, s, a);
-    hipLaunchKernelGGL(warm_attn_kernel<1>, dim3(T), blk_attn, 0, s, a);
-    if (a.dq || a.dw) hipLaunchKernelGGL(warm_dq_kernel, dim3(T), dim3(64 * (a.H_I / 16)), 0, s, a);
-  }
-  if (a.dk) {
-    const dim3 grid((a.max_len + kBK - 1) / kBK, a.nchunk, a.g.num_seqs);
-    if (a.H_I == 64) hipLaunchKernelGGL(warm_dk_kernel<2>, grid, dim3(256), 0, s, a);
-    else hipLaunchKernelGGL(warm_dk_kernel<1>, grid, dim3(256), 0, s, a);
-    const int64_t n4 = (int64_t)a.g.num_seqs * a.max_len * 32;
-    hipLaunchKernelGGL(warm_dk_reduce_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, s, a);
+  switch (stage) {
+    case 0:
+      if (T > 0) hipLaunchKernelGGL(warm_attn_kernel<0>, dim3(T), blk_attn, 0, s, a);
+      break;
+    case 1:
+      if (T > 0) hipLaunchKernelGGL(warm_attn_kernel<1>, dim3(T), blk_attn, 0, s, a);
+      break;
+    case 2:
+      if (T > 0 && (a.dq || a.dw)) hipLaunchKernelGGL(warm_dq_kernel, dim3(T), dim3(64 * (a.H_I / 16)), 0, s, a);
+      break;
+    case 3:
+      if (a.dk) {
+        const dim3 grid((a.max_len + kBK - 1) / kBK, a.nchunk, a.g.num_seqs);
+        if (a.H_I == 64) hipLaunchKernelGGL(warm_dk_kernel<2>, grid, dim3(256), 0, s, a);
+        else hipLaunchKernelGGL(warm_dk_kernel<1>, grid, dim3(256), 0, s, a);
+        const int64_t n4 = (int64_t)a.g.num_seqs * a.max_len * 32;
+        hipLaunchKernelGGL(warm_dk_reduce_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, s, a);
+      }
+      break;
+    default:
+      return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }

@@ -94,3 +94,6 @@ SMALL_WARMUP = PREFILL_32K.replace(name="warmup_L300", seq_len=300, seed=18, sam
 INT_WARMUP = PREFILL_32K.replace(name="warmup_L200_int", seq_len=200, seed=19, sample_rows=0,
                                  integer_indexer=True)
 RAGGED_WARMUP = PREFILL_32K.replace(name="warmup_b2_L260", seqs=2, seq_len=260, seed=20, sample_rows=0)
+
+# the warm-up objective's measured workload is selectable by name as well
+BY_NAME[WARMUP_4K.name] = WARMUP_4K
