@@ -154,6 +154,14 @@ def test_ragged_batch_of_last_rows():
     assert np.all(dk[1, 190:] == 0)
 
 
+def test_other_head_counts():
+    """H_I = 32 (one head pair per dk wave, two-wave dq workgroups) and H = 64 dense heads (four waves)."""
+    wl = workloads.SHAPES_WARMUP
+    announce("warm-up", wl.name)
+    inp = workloads.generate(wl, DEV)
+    _compare(inp, list(range(inp.num_rows)))
+
+
 def test_deterministic_and_forward_only():
     wl = workloads.SMALL_WARMUP
     announce("warm-up determinism", wl.name)

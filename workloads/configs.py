@@ -97,3 +97,5 @@ RAGGED_WARMUP = PREFILL_32K.replace(name="warmup_b2_L260", seqs=2, seq_len=260, 
 
 # the warm-up objective's measured workload is selectable by name as well
 BY_NAME[WARMUP_4K.name] = WARMUP_4K
+SHAPES_WARMUP = PREFILL_32K.replace(name="warmup_L230_hi32_h64", seq_len=230, seed=21, sample_rows=0,
+                                    H_I=32, H=64)
