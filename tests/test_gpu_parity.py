@@ -230,6 +230,21 @@ def test_topk_row_mode_long_rows(kind):
     _check_topk_rows(scores, lens, 2048, idx)
 
 
+@pytest.mark.parametrize("kind", ["normal", "ties", "signed_zeros", "all_equal", "sparse_ones"])
+@pytest.mark.parametrize("k", [64, 2048, 4096])
+def test_topk_row_mode_40k_rows(kind, k):
+    # > 512 rows of 17000-40000 candidates (row mode) for every score pattern
+    # and budget: boundary bins from a few keys (normal) to the whole row
+    # (all equal), candidates staged in LDS or read from global memory
+    announce("topk row mode 40k rows", kind, k)
+    lens = [40000 - 45 * i for i in range(520)]
+    batch = _decode_batch(lens)
+    scores = W.synthetic_scores(len(lens), 40000, kind, seed=11 + k, device=DEV)
+    idx = dsa.topk(batch, scores, k)
+    torch.cuda.synchronize()
+    _check_topk_rows(scores, lens, k, idx)
+
+
 # ------------------------------------------------------------------ fused decode
 
 @pytest.mark.parametrize("wl", [W.SMALL_DECODE, W.SMALL_PAGED], ids=lambda w: w.name)
