@@ -70,6 +70,46 @@ def _hip():
     return lib
 
 
+_ATTAINABLE = None
+
+
+def attainable_peaks():
+    """Measured reference peaks of this GPU, for fractions beside the vendor ones:
+    a plain 1 GiB device-to-device copy (bytes read + written per second) and a
+    bf16 8192^3 GEMM through torch (the vendor BLAS), each the best of 5."""
+    global _ATTAINABLE
+    if _ATTAINABLE is not None:
+        return _ATTAINABLE
+    import torch
+    n = 1 << 28                                   # 1 GiB of fp32
+    src = torch.empty(n, dtype=torch.float32, device="cuda:0").fill_(1.0)
+    dst = torch.empty_like(src)
+    a = torch.randn((8192, 8192), dtype=torch.bfloat16, device="cuda:0")
+    b = torch.randn((8192, 8192), dtype=torch.bfloat16, device="cuda:0")
+
+    def best(fn, reps=5):
+        fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            e1.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        return min(ts)
+
+    t_copy = best(lambda: dst.copy_(src))
+    t_gemm = best(lambda: torch.mm(a, b))
+    _ATTAINABLE = {"copy_GB/s": round(2 * n * 4 / (t_copy * 1e-3) / 1e9, 1),
+                   "gemm_bf16_TFLOP/s": round(2 * 8192 ** 3 / (t_gemm * 1e-3) / 1e12, 1),
+                   "how": "1 GiB device copy (read + write bytes); bf16 8192^3 torch.mm; best of 5"}
+    del src, dst, a, b
+    torch.cuda.empty_cache()
+    return _ATTAINABLE
+
+
 def decode_bytes_per_query(wl, ctx):
     """Algorithmic HBM bytes of one decode query over `ctx` cached tokens.
 
@@ -242,6 +282,9 @@ def run_bench(args):
                       "bf16_frac": round(att_flops / (stage_ms["attention"] * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)},
     }
     del ws, out, lse
+    att = attainable_peaks()
+    res["attainable"] = att
+    res["roofline"]["frac_of_attainable"] = round(idx_gbs / att["copy_GB/s"], 4)
     return res, inp
 
 
@@ -309,6 +352,7 @@ def run_prefill(args):
                     "bf16_peak_frac": round(idx_tf / BF16_PEAK_TFLOPS, 4)},
         "attention": {"selected_rows": att_rows, "TFLOP/s": round(att_tf, 1),
                       "bf16_peak_frac": round(att_tf / BF16_PEAK_TFLOPS, 4)},
+        "attainable": attainable_peaks(),
         "cpu_baseline": None,
     }
 
@@ -471,6 +515,9 @@ def run_warmup(args):
         "stages_tflops": {k: round(v, 1) for k, v in tfs.items()},
         "wall_s": round(elapsed, 3),
     }
+    att = attainable_peaks()
+    res["attainable"] = att
+    res["roofline"]["frac_of_attainable"] = round(tfs[dom] / att["gemm_bf16_TFLOP/s"], 4)
     if args.no_cpu_baseline:
         res["cpu_baseline"] = None
     else:

@@ -200,7 +200,7 @@ FusedPlan plan_fused(int T, int max_len, int k, int H, int D_v) {
 struct WarmPlan {
   int64_t ld = 0;
   int row_chunk = 0, nchunk = 0;
-  size_t off_scores = 0, off_lse = 0, off_dk = 0, bytes = 0;
+  size_t off_scores = 0, off_lse = 0, off_dk = 0, off_pairs = 0, bytes = 0;
 };
 
 WarmPlan plan_warmup(int T, int B, int max_len, int max_q, int H) {
@@ -216,6 +216,8 @@ WarmPlan plan_warmup(int T, int B, int max_len, int max_q, int H) {
   p.off_lse = o; o += (size_t)T * H * 4;
   o = (size_t)round_up((int64_t)o, 256);
   p.off_dk = o; o += (size_t)p.nchunk * B * max_len * 128 * 4;
+  o = (size_t)round_up((int64_t)o, 256);
+  p.off_pairs = o; o += (size_t)(B + 1) * 4;
   p.bytes = (size_t)round_up((int64_t)o, 256);
   return p;
 }
@@ -608,6 +610,7 @@ extern "C" dsa_status dsa_indexer_warmup(const dsa_batch* batch, const uint16_t*
   a.max_len = batch->max_len;
   a.row_chunk = p.row_chunk;
   a.nchunk = p.nchunk;
+  a.pair_start = reinterpret_cast<int*>(ws + p.off_pairs);
   for (int stage = 0; stage < 4; ++stage) {
     LAUNCH(launch_warmup(a, stage, s), "warm-up launch");
     LAUNCH(mark(2 + stage), "stage event");

@@ -115,6 +115,7 @@ struct WarmArgs {
   int max_len;
   int row_chunk;         // query rows per dk chunk
   int nchunk;
+  int* pair_start;       // [B + 1] first row pair of each sequence (the dense passes take two rows each)
 };
 
 // stage 0: dense log-sum-exp pass; 1: target, KL and dI; 2: dq and dw; 3: dk

@@ -14,7 +14,8 @@
 //   dk[s] = sum_t dI_t[s] sum_j w_t[j] q_scale_t [z_t[j,s] > 0] q8_t[j]   (w.r.t. k_scale*k8)
 //
 // Launch sequence (after the main path's prefill indexer wrote I):
-//   warm_attn_kernel<0>  per row and head, the log2-sum-exp2 of the scaled
+//   warm_attn_kernel<0>  per row and head (two adjacent rows of a sequence per
+//                        workgroup), the log2-sum-exp2 of the scaled
 //                        dense logits over the row's prefix (S = q K^T; each
 //                        lane reduces its keys online, lanes combine at the end);
 //   warm_attn_kernel<1>  recomputes the same logits with the same instructions,
@@ -92,29 +93,68 @@ constexpr int kWTile = kWRB * kWCH * 16;
 
 __device__ __forceinline__ int wswz(int r) { return (r >> 1) & 7; }
 
+// Pairs of adjacent query rows of one sequence: pair_start[b] = sum over
+// earlier sequences of ceil(nq / 2).  One workgroup, any number of sequences.
+__global__ void __launch_bounds__(256) warm_pairs_kernel(WarmArgs a) {
+  __shared__ uint32_t tmp[4];
+  uint32_t carry = 0;
+  for (int b0 = 0; b0 < a.g.num_seqs; b0 += 256) {
+    const int bb = b0 + (int)threadIdx.x;
+    const uint32_t c = bb < a.g.num_seqs ? (uint32_t)((a.g.q_start[bb + 1] - a.g.q_start[bb] + 1) >> 1) : 0u;
+    uint32_t tot;
+    const uint32_t ex = block_exclusive_scan<256>(c, tmp, tot);
+    if (bb < a.g.num_seqs) a.pair_start[bb] = (int)(carry + ex);
+    carry += tot;
+  }
+  if (threadIdx.x == 0) a.pair_start[a.g.num_seqs] = (int)carry;
+}
+
+// One workgroup per pair of adjacent query rows of a sequence (the last row of
+// a sequence with an odd row count is alone), H/16 waves of 16 heads.  The
+// longer row's prefix is streamed in 64-key blocks through a double-buffered
+// LDS tile filled by DMA (16-byte chunk c of key r at chunk position
+// c ^ ((r >> 1) & 7)); each K fragment read from the tile feeds the MFMAs of
+// both rows, and the shorter row masks the one key past its position.
 template <int MODE>
 __global__ void __launch_bounds__(512) warm_attn_kernel(WarmArgs a) {
   __shared__ __attribute__((aligned(16))) char ktile[2][kWTile];
-  __shared__ float hsum[8][kWRB];
-  __shared__ float red[2][8];
+  __shared__ float hsum[2][8][kWRB];
+  __shared__ float red[2][2][8];
 
   const int waves = blockDim.x >> 6;
-  const int t = a.g.num_rows - 1 - (int)blockIdx.x;     // long rows first
+  const int npairs = a.pair_start[a.g.num_seqs];
+  if ((int)blockIdx.x >= npairs) return;                 // uniform
+  const int g = npairs - 1 - (int)blockIdx.x;            // long rows first
+  int b;
+  {
+    int lo = 0, hi = a.g.num_seqs - 1;                   // last sequence with pair_start <= g
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (a.pair_start[mid] <= g) lo = mid; else hi = mid - 1;
+    }
+    b = lo;
+  }
+  const int nq = a.g.q_start[b + 1] - a.g.q_start[b];
+  const int i0 = 2 * (g - a.pair_start[b]);
+  const int tA = a.g.q_start[b] + i0;
+  const bool two = i0 + 1 < nq;                          // uniform
+  const int posA = a.g.seq_lens[b] - nq + i0;
+  const int n = posA + 1 + (two ? 1 : 0);                // keys of the longer row
+  const int tr[2] = {tA, tA + 1};
+  const int npos[2] = {posA + 1, posA + 2};              // keys each row sees
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int nl = lane & 15, grp = lane >> 4;
-  int b, pos;
-  row_seq_pos(a.g, t, b, pos);
-  const int n = pos + 1;
   const int nblk = (n + kWRB - 1) / kWRB;
   const int64_t row_base = (int64_t)b * a.kv.seq_stride;
 
-  // q fragments: head 16*wave + nl, dims 32*kk + 8*grp .. +7
-  v8bf qf[kWKK];
-  {
-    const uint16_t* qrow = a.q + ((int64_t)t * a.H + wave * 16 + nl) * kWD;
+  // q fragments of both rows: head 16*wave + nl, dims 32*kk + 8*grp .. +7
+  v8bf qf[2][kWKK];
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    const uint16_t* qrow = a.q + ((int64_t)(two ? tr[r] : tA) * a.H + wave * 16 + nl) * kWD;
 #pragma unroll
     for (int kk = 0; kk < kWKK; ++kk)
-      qf[kk] = __builtin_bit_cast(v8bf, *reinterpret_cast<const v4i*>(qrow + kk * 32 + grp * 8));
+      qf[r][kk] = __builtin_bit_cast(v8bf, *reinterpret_cast<const v4i*>(qrow + kk * 32 + grp * 8));
   }
 
   auto issue = [&](int blk) {
@@ -136,36 +176,50 @@ __global__ void __launch_bounds__(512) warm_attn_kernel(WarmArgs a) {
   const int kb0 = (nl * kWCH + ((0 + grp) ^ yk)) * 16;
   const int kb1 = (nl * kWCH + ((4 + grp) ^ yk)) * 16;
 
-  // MODE 0: per lane, heads 16*wave + 4*grp + i over keys 16*mt + nl of every
-  // block: online (max, sum) in log2 units, combined across the 16 lanes at the end
-  float m_run[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-  float l_run[4] = {0.f, 0.f, 0.f, 0.f};
-  // MODE 1: log2-sum-exp2 of heads 16*wave + 4*grp + i, the row's indexer score
-  // max and log2-sum-exp2 relative to it, the KL sum
-  float L[4] = {0.f, 0.f, 0.f, 0.f};
-  float mI = 0.0f, lseI2 = 0.0f, kl = 0.0f;
-  float* srow = a.scores + (int64_t)t * a.ld;
+  // MODE 0: per lane and row, heads 16*wave + 4*grp + i over keys 16*mt + nl of
+  // every block: online (max, sum) in log2 units, combined across the 16 lanes at the end
+  float m_run[2][4], l_run[2][4];
+#pragma unroll
+  for (int r = 0; r < 2; ++r)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      m_run[r][i] = -INFINITY;
+      l_run[r][i] = 0.0f;
+    }
+  // MODE 1: per row, the heads' log2-sum-exp2, the indexer score maximum and
+  // log2-sum-exp2 relative to it, and (in wave r, for row r) the KL sum
+  float L[2][4];
+  float mI[2] = {0.f, 0.f}, lseI2[2] = {0.f, 0.f};
+  float kl[2] = {0.f, 0.f};
+  const int nrows = two ? 2 : 1;
   if constexpr (MODE == 1) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) L[i] = a.lse2[(int64_t)t * a.H + wave * 16 + grp * 4 + i];
+    for (int r = 0; r < 2; ++r)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        L[r][i] = (r == 0 || two) ? a.lse2[(int64_t)tr[r] * a.H + wave * 16 + grp * 4 + i] : 0.0f;
     // softmax of the scores taken relative to their maximum: I - max is exact
     // near the top, so P keeps fp32 relative accuracy however large I is
-    float m = -INFINITY;
-    for (int s = threadIdx.x; s < n; s += blockDim.x) m = fmaxf(m, srow[s]);
-    m = wave_max(m);
-    if (lane == 0) red[0][wave] = m;
-    __syncthreads();
-    mI = red[0][0];
-    for (int w = 1; w < waves; ++w) mI = fmaxf(mI, red[0][w]);
-    float l = 0.0f;
-    for (int s = threadIdx.x; s < n; s += blockDim.x) l += __builtin_amdgcn_exp2f(__fmul_rn(srow[s] - mI, kLog2e));
+    for (int r = 0; r < (two ? 2 : 1); ++r) {
+      const float* srow = a.scores + (int64_t)tr[r] * a.ld;
+      float m = -INFINITY;
+      for (int s = threadIdx.x; s < npos[r]; s += blockDim.x) m = fmaxf(m, srow[s]);
+      m = wave_max(m);
+      if (lane == 0) red[r][0][wave] = m;
+      __syncthreads();
+      float mm = red[r][0][0];
+      for (int w = 1; w < waves; ++w) mm = fmaxf(mm, red[r][0][w]);
+      float l = 0.0f;
+      for (int s = threadIdx.x; s < npos[r]; s += blockDim.x) l += __builtin_amdgcn_exp2f(__fmul_rn(srow[s] - mm, kLog2e));
 #pragma unroll
-    for (int o = 1; o < 64; o <<= 1) l += __shfl_xor(l, o);
-    if (lane == 0) red[1][wave] = l;
-    __syncthreads();
-    float ll = 0.0f;
-    for (int w = 0; w < waves; ++w) ll += red[1][w];
-    lseI2 = __builtin_amdgcn_logf(ll);
+      for (int o = 1; o < 64; o <<= 1) l += __shfl_xor(l, o);
+      if (lane == 0) red[r][1][wave] = l;
+      __syncthreads();
+      float ll = 0.0f;
+      for (int w = 0; w < waves; ++w) ll += red[r][1][w];
+      mI[r] = mm;
+      lseI2[r] = __builtin_amdgcn_logf(ll);
+    }
   }
 
   issue(0);
@@ -175,62 +229,75 @@ __global__ void __launch_bounds__(512) warm_attn_kernel(WarmArgs a) {
     if (blk + 1 < nblk) issue(blk + 1);
     const char* kt = ktile[blk & 1];
 
-    v4f s[4];
+    // S = q K^T for both rows, D[head][key]; both passes run this same
+    // instruction sequence, so they see bit-identical logits
+    v4f s[2][4];
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) s[mt] = v4f{0.f, 0.f, 0.f, 0.f};
+    for (int r = 0; r < 2; ++r)
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) s[r][mt] = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kk = 0; kk < kWKK; ++kk) {
       v8bf kf[4];
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
         kf[mt] = *reinterpret_cast<const v8bf*>(kt + ((kk & 1) ? kb1 : kb0) + (kk >> 1) * 128 + mt * 16 * kWCH * 16);
-      // D[head][key]; both passes use this same instruction sequence, so they
-      // see bit-identical logits (and a row of one token gets a target of exactly 1)
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt) s[mt] = mfma(qf[kk], kf[mt], s[mt]);
+      for (int mt = 0; mt < 4; ++mt) s[0][mt] = mfma(qf[0][kk], kf[mt], s[0][mt]);
+      if (two) {
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) s[1][mt] = mfma(qf[1][kk], kf[mt], s[1][mt]);
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
 
     if constexpr (MODE == 0) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float x[4];
-        float mx = -INFINITY;
+      for (int r = 0; r < 2; ++r) {
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt) {
-          const int key = blk * kWRB + mt * 16 + nl;
-          x[mt] = key < n ? __fmul_rn(s[mt][i], a.scale_log2) : -INFINITY;
-          mx = fmaxf(mx, x[mt]);
+        for (int i = 0; i < 4; ++i) {
+          float x[4];
+          float mx = -INFINITY;
+#pragma unroll
+          for (int mt = 0; mt < 4; ++mt) {
+            const int key = blk * kWRB + mt * 16 + nl;
+            x[mt] = key < npos[r] ? __fmul_rn(s[r][mt][i], a.scale_log2) : -INFINITY;
+            mx = fmaxf(mx, x[mt]);
+          }
+          const float m_new = fmaxf(m_run[r][i], mx);
+          const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
+          float acc = l_run[r][i] * __builtin_amdgcn_exp2f(m_run[r][i] - m_use);
+#pragma unroll
+          for (int mt = 0; mt < 4; ++mt) acc += __builtin_amdgcn_exp2f(x[mt] - m_use);
+          l_run[r][i] = acc;
+          m_run[r][i] = m_new;
         }
-        const float m_new = fmaxf(m_run[i], mx);
-        const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
-        float acc = l_run[i] * __builtin_amdgcn_exp2f(m_run[i] - m_use);
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt) acc += __builtin_amdgcn_exp2f(x[mt] - m_use);
-        l_run[i] = acc;
-        m_run[i] = m_new;
       }
     } else {
       // sum over this wave's 16 heads of exp2(x - lse): in-lane over i, then over lane groups
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
-        float e = 0.0f;
+      for (int r = 0; r < 2; ++r) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) e += __builtin_amdgcn_exp2f(__fmul_rn(s[mt][i], a.scale_log2) - L[i]);
-        e = wsum4(e);
-        if (grp == 0) hsum[wave][mt * 16 + nl] = e;
+        for (int mt = 0; mt < 4; ++mt) {
+          float e = 0.0f;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) e += __builtin_amdgcn_exp2f(__fmul_rn(s[r][mt][i], a.scale_log2) - L[r][i]);
+          e = wsum4(e);
+          if (grp == 0) hsum[r][wave][mt * 16 + nl] = e;
+        }
       }
       lds_barrier();
-      if (wave == 0) {
+      for (int r = wave; r < nrows; r += waves) {       // wave r turns row r's keys into a, P, KL and dI
         const int key = blk * kWRB + lane;
-        if (key < n) {
+        if (key < npos[r]) {
           float hs = 0.0f;
-          for (int w = 0; w < waves; ++w) hs += hsum[w][lane];
-          const float at = hs * a.inv_H;                  // target probability
-          const float lp = __fmul_rn(srow[key] - mI, kLog2e) - lseI2;    // log2 P
+          for (int w = 0; w < waves; ++w) hs += hsum[r][w][lane];
+          float* srow = a.scores + (int64_t)tr[r] * a.ld;
+          const float at = hs * a.inv_H;                          // target probability
+          const float lp = __fmul_rn(srow[key] - mI[r], kLog2e) - lseI2[r];    // log2 P
           const float pm = __builtin_amdgcn_exp2f(lp);
-          srow[key] = pm - at;                            // dI, written over the score
-          if (at > 0.0f) kl += at * (__builtin_amdgcn_logf(at) - lp);
+          srow[key] = pm - at;                                    // dI, written over the score
+          if (at > 0.0f) kl[r] += at * (__builtin_amdgcn_logf(at) - lp);
         }
       }
     }
@@ -239,24 +306,29 @@ __global__ void __launch_bounds__(512) warm_attn_kernel(WarmArgs a) {
   if constexpr (MODE == 0) {
     // combine the 16 lanes of the group that hold heads 4*grp + i
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float m = m_run[i], l = l_run[i];
+    for (int r = 0; r < 2; ++r) {
 #pragma unroll
-      for (int o = 1; o < 16; o <<= 1) {
-        const float m2 = __shfl_xor(m, o), l2 = __shfl_xor(l, o);
-        const float mm = fmaxf(m, m2);
-        const float a1 = (m == -INFINITY) ? 0.0f : l * __builtin_amdgcn_exp2f(m - mm);
-        const float a2 = (m2 == -INFINITY) ? 0.0f : l2 * __builtin_amdgcn_exp2f(m2 - mm);
-        m = mm;
-        l = a1 + a2;
+      for (int i = 0; i < 4; ++i) {
+        float m = m_run[r][i], l = l_run[r][i];
+#pragma unroll
+        for (int o = 1; o < 16; o <<= 1) {
+          const float m2 = __shfl_xor(m, o), l2 = __shfl_xor(l, o);
+          const float mm = fmaxf(m, m2);
+          const float a1 = (m == -INFINITY) ? 0.0f : l * __builtin_amdgcn_exp2f(m - mm);
+          const float a2 = (m2 == -INFINITY) ? 0.0f : l2 * __builtin_amdgcn_exp2f(m2 - mm);
+          m = mm;
+          l = a1 + a2;
+        }
+        if (nl == 0 && (r == 0 || two))
+          a.lse2[(int64_t)tr[r] * a.H + wave * 16 + grp * 4 + i] = m + __builtin_amdgcn_logf(l);
       }
-      if (nl == 0) a.lse2[(int64_t)t * a.H + wave * 16 + grp * 4 + i] = m + __builtin_amdgcn_logf(l);
     }
   } else {
-    if (wave == 0) {
+    for (int r = wave; r < nrows; r += waves) {
+      float v = kl[r];
 #pragma unroll
-      for (int o = 1; o < 64; o <<= 1) kl += __shfl_xor(kl, o);
-      if (lane == 0) a.loss[t] = kl * kLn2;
+      for (int o = 1; o < 64; o <<= 1) v += __shfl_xor(v, o);
+      if (lane == 0) a.loss[tr[r]] = v * kLn2;
     }
   }
 }
@@ -594,10 +666,13 @@ hipError_t launch_warmup(const WarmArgs& a, int stage, hipStream_t s) {
   const dim3 blk_attn(64 * (a.H / 16));
   switch (stage) {
     case 0:
-      if (T > 0) hipLaunchKernelGGL(warm_attn_kernel<0>, dim3(T), blk_attn, 0, s, a);
+      if (T > 0) {
+        hipLaunchKernelGGL(warm_pairs_kernel, dim3(1), dim3(256), 0, s, a);
+        hipLaunchKernelGGL(warm_attn_kernel<0>, dim3((T + a.g.num_seqs + 1) / 2), blk_attn, 0, s, a);
+      }
       break;
     case 1:
-      if (T > 0) hipLaunchKernelGGL(warm_attn_kernel<1>, dim3(T), blk_attn, 0, s, a);
+      if (T > 0) hipLaunchKernelGGL(warm_attn_kernel<1>, dim3((T + a.g.num_seqs + 1) / 2), blk_attn, 0, s, a);
       break;
     case 2:
       if (T > 0 && (a.dq || a.dw)) hipLaunchKernelGGL(warm_dq_kernel, dim3(T), dim3(64 * (a.H_I / 16)), 0, s, a);

@@ -162,6 +162,19 @@ def test_other_head_counts():
     _compare(inp, list(range(inp.num_rows)))
 
 
+def test_odd_row_counts_and_one_wave():
+    """An odd number of rows (the last one has no partner) with H = 16 (one wave per workgroup),
+    and a ragged pair of sequences with odd row counts."""
+    wl = workloads.ONEWAVE_WARMUP
+    announce("warm-up", wl.name)
+    inp = workloads.generate(wl, DEV)
+    _compare(inp, list(range(inp.num_rows)))
+    wl = workloads.RAGGED_WARMUP
+    announce("warm-up", wl.name, "lens (260, 191), rows (71, 191)")
+    inp = _ragged(workloads.generate(wl, DEV), [260, 191], [71, 191])
+    _compare(inp, list(range(inp.num_rows)))
+
+
 def test_deterministic_and_forward_only():
     wl = workloads.SMALL_WARMUP
     announce("warm-up determinism", wl.name)

@@ -99,3 +99,4 @@ RAGGED_WARMUP = PREFILL_32K.replace(name="warmup_b2_L260", seqs=2, seq_len=260, 
 BY_NAME[WARMUP_4K.name] = WARMUP_4K
 SHAPES_WARMUP = PREFILL_32K.replace(name="warmup_L230_hi32_h64", seq_len=230, seed=21, sample_rows=0,
                                     H_I=32, H=64)
+ONEWAVE_WARMUP = PREFILL_32K.replace(name="warmup_L151_h16", seq_len=151, seed=22, sample_rows=0, H=16)
