@@ -36,9 +36,9 @@ BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, vendor figure
 INDEXER_COUNTERS = {
     "sources": ["sparse_attention_long_06_amd/csrc/indexer.hip", "sparse_attention_long_06_amd/csrc/dsa_common.h",
                 "sparse_attention_long_06_amd/csrc/dsa_kernels.h", "sparse_attention_long_06_amd/csrc/api.hip"],
-    "sha256": "ae8c7ee80fb679ffbe8e46e23942bf084f3526c6f5aa383c482c631f45b1f2d4",
-    "fetch_kib": 272632.6,
-    "write_kib": 17231.0,
+    "sha256": "5ad42d27fe45a3b21d1fda0003c16175fd0d6b45b6cab22869debf565a5f6cd2",
+    "fetch_kib": 272625.8,
+    "write_kib": 17230.9,
     "fetch_scale": 2.0,
     "write_scale": 1.0,
 }

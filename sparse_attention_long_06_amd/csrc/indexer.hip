@@ -569,8 +569,11 @@ __global__ void __launch_bounds__(256) indexer_prefill_ring_kernel(IndexerArgs a
       const int s0 = sbase + 16 * wave;              // this wave's 16 scales
       const int last = kend - 1 - s0;
       const uint32_t dst = slot + (uint32_t)(kPreKeys * DI + 64 * wave);
-      if (last >= 15 && off32 && !a.g.block_table) {
-        const char* sb = a.ksc.data + ((int64_t)b * a.ksc.seq_stride + s0) * a.ksc.row_stride;
+      if (last >= 15 && off32) {
+        // 16 keys never straddle a page; the page comes from a scalar lookup,
+        // which leaves the vector-memory counter of the ring alone
+        const int64_t srow = a.g.block_table ? row_of(s0) : (int64_t)b * a.ksc.seq_stride + s0;
+        const char* sb = a.ksc.data + srow * a.ksc.row_stride;
         if (lane < 16)
           asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, %2"
                        :: "s"(dst), "v"(soff), "s"(sb) : "memory");

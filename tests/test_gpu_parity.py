@@ -81,6 +81,11 @@ VARIANTS = [
     W.SMALL_DECODE.replace(name="decode_b3_ctx5000_k4096_hi16_di32", k=4096, H_I=16, d_I=32, seed=23),
     W.SMALL_PAGED.replace(name="paged_decode_b5_mixed100_6000_k1024", k=1024, seed=24),
     W.SMALL_PREFILL.replace(name="prefill_L2500_k512_hi8", k=512, H_I=8, seed=25),
+    # paged caches under the prefill layout: the prefill indexer's page lookups
+    # (8-key groups, ragged ends) and the attention gather through the table
+    W.SMALL_PREFILL.replace(name="prefill_b2_L2300_paged64", seqs=2, seq_len=2300, paged=True, block_size=64,
+                            seed=26),
+    W.SMALL_PREFILL.replace(name="prefill_L2100_paged16", seq_len=2100, paged=True, block_size=16, seed=27),
 ]
 
 
