@@ -617,8 +617,8 @@ def main():
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(json.dumps({"error": "this build measures one GPU only: the DSA path here has no multi-GPU "
-                                   "mode (see DESIGN.md for how it would shard); run with --gpus 1"}))
+        print(json.dumps({"error": "this benchmark runs on one GPU only: the DSA path has no multi-GPU mode "
+                                   "(sequences or key ranges would be sharded across GPUs); run with --gpus 1"}))
         raise SystemExit(2)
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
