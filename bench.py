@@ -34,6 +34,7 @@ BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, vendor figure
 # 1 GiB device copy: fetch x2.0, write x1.0.  The figures hold only for the
 # kernel sources they were taken on; any change to them reports null.
 INDEXER_COUNTERS = {
+    "workload": "decode_b32_ctx128k",
     "sources": ["sparse_attention_long_06_amd/csrc/indexer.hip", "sparse_attention_long_06_amd/csrc/dsa_common.h",
                 "sparse_attention_long_06_amd/csrc/dsa_kernels.h", "sparse_attention_long_06_amd/csrc/api.hip"],
     "sha256": "5ad42d27fe45a3b21d1fda0003c16175fd0d6b45b6cab22869debf565a5f6cd2",
@@ -53,10 +54,11 @@ def indexer_sources_sha256() -> str:
     return h.hexdigest()
 
 
-def indexer_traffic_bytes():
-    """Counter-measured HBM bytes per indexer launch, or None if the sources changed since."""
+def indexer_traffic_bytes(workload="decode_b32_ctx128k"):
+    """Counter-measured HBM bytes per indexer launch on the workload the counters
+    were taken on, or None (another workload, or the sources changed since)."""
     c = INDEXER_COUNTERS
-    if c["sha256"] is None or c["sha256"] != indexer_sources_sha256():
+    if workload != c["workload"] or c["sha256"] is None or c["sha256"] != indexer_sources_sha256():
         return None
     return int(round(c["fetch_kib"] * 1024 * c["fetch_scale"] + c["write_kib"] * 1024 * c["write_scale"]))
 
@@ -275,7 +277,7 @@ def run_bench(args):
         "context_tokens_scanned_per_s": round(ctx_total / (elapsed / args.steps), 1),
         "roofline": {"bound": "hbm", "kernel": "indexer_decode_ring_kernel (decode indexer + first top-k histogram)",
                      "achieved": round(idx_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(idx_gbs / HBM_PEAK_GBS, 4), "traffic": indexer_traffic_bytes(),
+                     "frac": round(idx_gbs / HBM_PEAK_GBS, 4), "traffic": indexer_traffic_bytes(wl.name),
                      "bytes_per_launch": idx_bytes, "launch_ms": round(stage_ms["indexer"], 4)},
         "stages_ms": {k: round(v, 4) for k, v in stage_ms.items()},
         "ms_per_step_with_stage_events": round(staged_ms, 4),

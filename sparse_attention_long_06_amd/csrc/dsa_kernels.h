@@ -29,7 +29,7 @@ struct IndexerArgs {
 constexpr int kIdxRowsPerWave = 2;
 constexpr int kIdxPrefillRows = 4 * kIdxRowsPerWave;
 constexpr int kIdxPrefillChunk = 1024;
-constexpr int kIdxDecodeChunk = 4096;
+constexpr int kIdxDecodeChunk = 2048;
 
 hipError_t launch_indexer(const IndexerArgs& a, int d_I, bool decode_layout, bool with_hist,
                           hipStream_t stream);
