@@ -117,7 +117,9 @@ TopkPlan plan_topk(int T, int max_len, int k) {
   TopkPlan p;
   if (T > kTopkSplitMaxRows || max_len <= k || T == 0) return p;
   p.split = true;
-  const int target = (kTopkSplitMaxRows + T - 1) / T;           // slices per row for ~512 workgroups
+  // slices per row: ~512 workgroups over the batch, and at least 16 per row so
+  // that rows shorter than max_len (mixed-length batches) still spread out
+  const int target = max((kTopkSplitMaxRows + T - 1) / T, 16);
   int slice = (int)round_up((max_len + target - 1) / target, 1024);
   if (slice < 1024) slice = 1024;
   int ns = (max_len + slice - 1) / slice;

@@ -211,6 +211,21 @@ def test_topk_split_mode_bit_exact(kind, k):
     _check_topk_rows(scores, lens, k, idx)
 
 
+@pytest.mark.parametrize("kind", ["normal", "ties", "all_equal"])
+def test_topk_split_mode_many_mixed_rows(kind):
+    # 200 rows of 2049-40000 candidates: split mode with 16 slices per row, so
+    # the short rows leave most of their slices empty
+    announce("topk split mode mixed rows", kind)
+    rng = np.random.default_rng(5)
+    lens = [int(x) for x in rng.integers(2049, 40001, size=200)]
+    lens[0], lens[1] = 40000, 2049
+    batch = _decode_batch(lens)
+    scores = W.synthetic_scores(len(lens), 40000, kind, seed=23, device=DEV)
+    idx = dsa.topk(batch, scores, 2048)
+    torch.cuda.synchronize()
+    _check_topk_rows(scores, lens, 2048, idx)
+
+
 @pytest.mark.parametrize("kind", ["normal", "ties", "signed_zeros", "sparse_ones"])
 def test_topk_row_mode_bit_exact(kind):
     announce("topk row mode", kind)
