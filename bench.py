@@ -37,9 +37,9 @@ INDEXER_COUNTERS = {
     "workload": "decode_b32_ctx128k",
     "sources": ["sparse_attention_long_06_amd/csrc/indexer.hip", "sparse_attention_long_06_amd/csrc/dsa_common.h",
                 "sparse_attention_long_06_amd/csrc/dsa_kernels.h", "sparse_attention_long_06_amd/csrc/api.hip"],
-    "sha256": "5ad42d27fe45a3b21d1fda0003c16175fd0d6b45b6cab22869debf565a5f6cd2",
-    "fetch_kib": 272625.8,
-    "write_kib": 17230.9,
+    "sha256": "bd09ef1138121d5f279aebb40c71fed797b6eceda9736cf3b6c1c186393804e1",
+    "fetch_kib": 272627.7,
+    "write_kib": 17231.1,
     "fetch_scale": 2.0,
     "write_scale": 1.0,
 }
