@@ -75,21 +75,61 @@ def _hip():
 _ATTAINABLE = None
 
 
+PROBES_LIB = os.path.join(ROOT, "sparse_attention_long_06_amd", "libdsa_probes.so")
+
+
+def _probes():
+    """ctypes view of libdsa_probes.so (include/dsa_probes.h); raises if it is not built."""
+    if not os.path.exists(PROBES_LIB):
+        raise RuntimeError(f"{PROBES_LIB} is missing: run `python -m sparse_attention_long_06_amd.build` first")
+    lib = ctypes.CDLL(PROBES_LIB)
+    vp, i64 = ctypes.c_void_p, ctypes.c_int64
+    lib.dsa_probe_stream_read.argtypes = [vp, i64, vp, i64, vp]
+    lib.dsa_probe_stream_read.restype = ctypes.c_int
+    lib.dsa_probe_stream_read_sink_words.argtypes = [i64]
+    lib.dsa_probe_stream_read_sink_words.restype = i64
+    lib.dsa_probe_mfma.argtypes = [ctypes.c_int, ctypes.c_int, vp, i64, vp]
+    lib.dsa_probe_mfma.restype = ctypes.c_int
+    lib.dsa_probe_mfma_sink_words.restype = i64
+    lib.dsa_probe_mfma_flops.argtypes = [ctypes.c_int, ctypes.c_int]
+    lib.dsa_probe_mfma_flops.restype = ctypes.c_double
+    return lib
+
+
 def attainable_peaks():
-    """Measured reference peaks of this GPU, for fractions beside the vendor ones:
-    a plain 1 GiB device-to-device copy (bytes read + written per second), a
-    1 GiB sum (bytes read per second) and a bf16 8192^3 GEMM through torch (the
-    vendor BLAS), each the best of 5.  The HBM reference is the larger of the
-    two streams."""
+    """Measured reference peaks of this GPU, for fractions beside the vendor ones,
+    each the best of 5:
+      * HBM: a streaming read of 1 GiB through the DMA-to-LDS path of the decode
+        indexer (libdsa_probes.so), a plain 1 GiB device-to-device copy (bytes
+        read + written per second) and a 1 GiB torch sum (bytes read per
+        second); the HBM reference is the largest of the three;
+      * matrix cores: an issue loop of independent bf16 MFMAs in each of the two
+        forms the kernels use (v_mfma_f32_16x16x32_bf16, v_mfma_f32_32x32x16_bf16)
+        and a bf16 8192^3 GEMM through torch (the vendor BLAS)."""
     global _ATTAINABLE
     if _ATTAINABLE is not None:
         return _ATTAINABLE
     import torch
+    probes = _probes()
     n = 1 << 28                                   # 1 GiB of fp32
     src = torch.empty(n, dtype=torch.float32, device="cuda:0").fill_(1.0)
     dst = torch.empty_like(src)
     a = torch.randn((8192, 8192), dtype=torch.bfloat16, device="cuda:0")
     b = torch.randn((8192, 8192), dtype=torch.bfloat16, device="cuda:0")
+    nbytes = n * 4
+    sink_r = torch.empty(probes.dsa_probe_stream_read_sink_words(nbytes), dtype=torch.int32, device="cuda:0")
+    sink_m = torch.empty(probes.dsa_probe_mfma_sink_words(), dtype=torch.float32, device="cuda:0")
+    mfma_iters = 4096
+
+    def stream_read():
+        st = torch.cuda.current_stream().cuda_stream
+        rc = probes.dsa_probe_stream_read(src.data_ptr(), nbytes, sink_r.data_ptr(), sink_r.numel(), st)
+        assert rc == 0, f"dsa_probe_stream_read returned {rc}"
+
+    def mfma(form):
+        st = torch.cuda.current_stream().cuda_stream
+        rc = probes.dsa_probe_mfma(form, mfma_iters, sink_m.data_ptr(), sink_m.numel(), st)
+        assert rc == 0, f"dsa_probe_mfma returned {rc}"
 
     def best(fn, reps=5):
         fn()
@@ -104,17 +144,25 @@ def attainable_peaks():
             ts.append(e0.elapsed_time(e1))
         return min(ts)
 
+    t_stream = best(stream_read)
     t_copy = best(lambda: dst.copy_(src))
     t_sum = best(lambda: src.sum())
+    t_m16 = best(lambda: mfma(0))
+    t_m32 = best(lambda: mfma(1))
     t_gemm = best(lambda: torch.mm(a, b))
-    copy_gbs = 2 * n * 4 / (t_copy * 1e-3) / 1e9
-    read_gbs = n * 4 / (t_sum * 1e-3) / 1e9
-    _ATTAINABLE = {"copy_GB/s": round(copy_gbs, 1), "read_GB/s": round(read_gbs, 1),
-                   "hbm_GB/s": round(max(copy_gbs, read_gbs), 1),
+    stream_gbs = nbytes / (t_stream * 1e-3) / 1e9
+    copy_gbs = 2 * nbytes / (t_copy * 1e-3) / 1e9
+    read_gbs = nbytes / (t_sum * 1e-3) / 1e9
+    m16 = probes.dsa_probe_mfma_flops(0, mfma_iters) / (t_m16 * 1e-3) / 1e12
+    m32 = probes.dsa_probe_mfma_flops(1, mfma_iters) / (t_m32 * 1e-3) / 1e12
+    _ATTAINABLE = {"stream_read_GB/s": round(stream_gbs, 1), "copy_GB/s": round(copy_gbs, 1),
+                   "read_GB/s": round(read_gbs, 1), "hbm_GB/s": round(max(stream_gbs, copy_gbs, read_gbs), 1),
+                   "mfma_16x16x32_bf16_TFLOP/s": round(m16, 1), "mfma_32x32x16_bf16_TFLOP/s": round(m32, 1),
                    "gemm_bf16_TFLOP/s": round(2 * 8192 ** 3 / (t_gemm * 1e-3) / 1e12, 1),
-                   "how": "1 GiB device copy (read + write bytes) and 1 GiB torch sum (read bytes); "
-                          "bf16 8192^3 torch.mm; best of 5"}
-    del src, dst, a, b
+                   "how": "1 GiB streaming read by LDS DMA (dsa_probe_stream_read), 1 GiB device copy "
+                          "(read + write bytes), 1 GiB torch sum (read bytes); independent bf16 MFMA chains "
+                          "(dsa_probe_mfma); bf16 8192^3 torch.mm; best of 5"}
+    del src, dst, a, b, sink_r, sink_m
     torch.cuda.empty_cache()
     return _ATTAINABLE
 
@@ -526,7 +574,8 @@ def run_warmup(args):
     }
     att = attainable_peaks()
     res["attainable"] = att
-    res["roofline"]["frac_of_attainable"] = round(tfs[dom] / att["gemm_bf16_TFLOP/s"], 4)
+    # the warm-up kernels run on v_mfma_f32_16x16x32_bf16: that form's measured rate
+    res["roofline"]["frac_of_attainable"] = round(tfs[dom] / att["mfma_16x16x32_bf16_TFLOP/s"], 4)
     if args.no_cpu_baseline:
         res["cpu_baseline"] = None
     else:

@@ -210,3 +210,53 @@ def test_warmup_validation(lib):
     # the workspace size ignores k and needs q_start
     assert lib.dsa_workspace_size(_lib.DSA_WS_WARMUP, ctypes.byref(pre), 99999, 128, 0) == need
     assert lib.dsa_workspace_size(_lib.DSA_WS_WARMUP, ctypes.byref(_batch()), 0, 128, 0) == ctypes.c_size_t(-1).value
+
+
+# ---------------------------------------------------------------- attainable-peak probes (bench references)
+
+PROBES_HEADER = os.path.join(ROOT, "include", "dsa_probes.h")
+PROBES_LIB = os.path.join(ROOT, "sparse_attention_long_06_amd", "libdsa_probes.so")
+
+
+@pytest.fixture(scope="module")
+def probes():
+    if not os.path.exists(PROBES_LIB):
+        from sparse_attention_long_06_amd import build
+        build.build()
+    lib = ctypes.CDLL(PROBES_LIB)
+    vp, i64 = ctypes.c_void_p, ctypes.c_int64
+    lib.dsa_probe_stream_read.argtypes = [vp, i64, vp, i64, vp]
+    lib.dsa_probe_stream_read_sink_words.argtypes = [i64]
+    lib.dsa_probe_stream_read_sink_words.restype = i64
+    lib.dsa_probe_mfma.argtypes = [ctypes.c_int, ctypes.c_int, vp, i64, vp]
+    lib.dsa_probe_mfma_sink_words.restype = i64
+    lib.dsa_probe_mfma_flops.argtypes = [ctypes.c_int, ctypes.c_int]
+    lib.dsa_probe_mfma_flops.restype = ctypes.c_double
+    return lib
+
+
+def test_probe_library_exports_every_declared_symbol(probes):
+    txt = re.sub(r"/\*.*?\*/", "", open(PROBES_HEADER).read(), flags=re.S)
+    names = sorted(set(re.findall(r"\b(dsa_[a-z_]+)\s*\(", txt)))
+    assert names == ["dsa_probe_mfma", "dsa_probe_mfma_flops", "dsa_probe_mfma_sink_words",
+                     "dsa_probe_stream_read", "dsa_probe_stream_read_sink_words"]
+    for n in names:
+        assert hasattr(probes, n), n
+
+
+def test_probe_sizes_and_argument_checks(probes):
+    # 257 tiles of 2 KiB: two workgroups of 256 threads
+    assert probes.dsa_probe_stream_read_sink_words(2048 * 257) == 512
+    assert probes.dsa_probe_stream_read_sink_words(1000) == -1
+    assert probes.dsa_probe_mfma_flops(0, 3) == 2048 * 4 * 3 * 8 * (2 * 16 * 16 * 32)
+    assert probes.dsa_probe_mfma_flops(1, 3) == 2048 * 4 * 3 * 4 * (2 * 32 * 32 * 16)
+    assert probes.dsa_probe_mfma_flops(2, 3) == -1
+    big = 1 << 30
+    # every case fails validation before any launch
+    assert probes.dsa_probe_stream_read(None, 2048, FAKE, big, None) == -1
+    assert probes.dsa_probe_stream_read(FAKE, 1000, FAKE, big, None) == -1
+    assert probes.dsa_probe_stream_read(FAKE + 4, 2048, FAKE, big, None) == -1
+    assert probes.dsa_probe_stream_read(FAKE, 2048 * 257, FAKE, 511, None) == -1
+    assert probes.dsa_probe_mfma(2, 10, FAKE, big, None) == -1
+    assert probes.dsa_probe_mfma(0, 0, FAKE, big, None) == -1
+    assert probes.dsa_probe_mfma(1, 10, FAKE, probes.dsa_probe_mfma_sink_words() - 1, None) == -1
