@@ -504,22 +504,35 @@ __global__ void __launch_bounds__(kFinalNT) topk_finalize_kernel(TopkArgs a) {
   const uint2* rowlists = a.lists + (int64_t)t * a.nslices * a.slice;
   const SegSrc gs{rowlists, offs, a.nslices, a.slice};
   if (m <= (uint32_t)kSplitCap) {
-    for (int base = 0; base < (int)m; base += kFinalNT * 4 * kUnr) {
-      uint32_t key[kUnr][4];
-      int id[kUnr][4];
-      bool ok[kUnr][4];
+    // Stage the concatenated lists slice by slice: 32 threads per slice copy
+    // its (key, index) pairs two at a time (16-byte loads, kUnr in flight
+    // per thread) to their place after the earlier slices' candidates.
+    constexpr int GROUPS = kFinalNT / 32;
+    const int l32 = threadIdx.x & 31;
+    for (int sl = threadIdx.x >> 5; sl < a.nslices; sl += GROUPS) {
+      const uint4* src = reinterpret_cast<const uint4*>(rowlists + (int64_t)sl * a.slice);
+      const uint32_t o = offs[sl], c = cnt[sl];
+      const uint32_t npairs = (c + 1) >> 1;         // an odd count reads one unused entry of its region
+      for (uint32_t p0 = 0; p0 < npairs; p0 += 32 * kUnr) {
+        uint4 v[kUnr];
 #pragma unroll
-      for (int u = 0; u < kUnr; ++u) gs.load4(base + (u * kFinalNT + threadIdx.x) * 4, key[u], id[u], ok[u]);
+        for (int u = 0; u < kUnr; ++u) {
+          const uint32_t pp = p0 + u * 32 + l32;
+          v[u] = pp < npairs ? src[pp] : make_uint4(0u, 0u, 0u, 0u);
+        }
 #pragma unroll
-      for (int u = 0; u < kUnr; ++u)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int p = base + (u * kFinalNT + threadIdx.x) * 4 + j;
-          if (ok[u][j]) {
-            lkey[p] = key[u][j];
-            lidx[p] = id[u][j];
+        for (int u = 0; u < kUnr; ++u) {
+          const uint32_t e = 2 * (p0 + u * 32 + l32);
+          if (e < c) {
+            lkey[o + e] = v[u].x;
+            lidx[o + e] = (int)v[u].y;
+          }
+          if (e + 1 < c) {
+            lkey[o + e + 1] = v[u].z;
+            lidx[o + e + 1] = (int)v[u].w;
           }
         }
+      }
     }
     lds_barrier();
     const LdsSrc ls{lkey, lidx, (int)m};
