@@ -38,8 +38,8 @@ INDEXER_COUNTERS = {
     "sources": ["sparse_attention_long_06_amd/csrc/indexer.hip", "sparse_attention_long_06_amd/csrc/dsa_common.h",
                 "sparse_attention_long_06_amd/csrc/dsa_kernels.h", "sparse_attention_long_06_amd/csrc/api.hip"],
     "sha256": "bd09ef1138121d5f279aebb40c71fed797b6eceda9736cf3b6c1c186393804e1",
-    "fetch_kib": 272627.7,
-    "write_kib": 17231.1,
+    "fetch_kib": 272608.1,
+    "write_kib": 17231.0,
     "fetch_scale": 2.0,
     "write_scale": 1.0,
 }
