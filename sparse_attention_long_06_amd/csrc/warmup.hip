@@ -551,34 +551,55 @@ __global__ void __launch_bounds__(256) warm_dk_kernel(WarmArgs a) {
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) dk[mt][dt] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  for (int i0 = ibeg; i0 < iend; i0 += RPS) {
-    lds_barrier();
-    // stage q8 rows (bf16), dI over the key tile, w * q_scale
-    for (int it = threadIdx.x; it < RPS * HI * 8; it += 256) {
+  // The next step's q8 rows, dI over the key tile and w * q_scale are loaded
+  // into registers while the current step computes (the loads' latency would
+  // otherwise open every step), then widened into LDS at the top of the next.
+  constexpr int QI = RPS * HI * 8 / 256;      // 16-byte q8 chunks per thread per step
+  static_assert(RPS * HI * 8 == QI * 256 && RPS * kBK <= 256 && RPS * HI <= 256, "staging split");
+  v4i qpre[QI];
+  float gpre = 0.0f, wpre = 0.0f;
+  auto load_step = [&](int i0) {
+#pragma unroll
+    for (int u = 0; u < QI; ++u) {
+      const int it = u * 256 + (int)threadIdx.x;
       const int rr = it / (HI * 8), rem = it % (HI * 8);
-      const int h = rem >> 3, c8 = rem & 7;      // head, 16-byte fp8 chunk
+      const int h = rem >> 3, c8 = rem & 7;     // head, 16-byte fp8 chunk
       const int i = min(i0 + rr, iend - 1);
-      const v4i v = *reinterpret_cast<const v4i*>(a.q8 + ((int64_t)(r0 + i) * a.H_I + h) * 128 + 16 * c8);
+      qpre[u] = *reinterpret_cast<const v4i*>(a.q8 + ((int64_t)(r0 + i) * a.H_I + h) * 128 + 16 * c8);
+    }
+    if ((int)threadIdx.x < RPS * kBK) {
+      const int rr = threadIdx.x / kBK, kk = threadIdx.x % kBK;
+      const int i = i0 + rr;
+      const int s = s0 + kk;
+      gpre = (i < iend && s <= base + i) ? a.scores[(int64_t)(r0 + i) * a.ld + s] : 0.0f;
+    }
+    if ((int)threadIdx.x < RPS * HI) {
+      const int rr = threadIdx.x / HI, h = threadIdx.x % HI;
+      const int i = min(i0 + rr, iend - 1);
+      const float qs = a.q_scale ? a.q_scale[r0 + i] : 1.0f;
+      wpre = a.w[(int64_t)(r0 + i) * a.H_I + h] * qs;
+    }
+  };
+  load_step(ibeg);
+
+  for (int i0 = ibeg; i0 < iend; i0 += RPS) {
+    lds_barrier();                              // every wave is done with the previous step's tiles
+    // stage q8 rows (bf16), dI over the key tile, w * q_scale
+#pragma unroll
+    for (int u = 0; u < QI; ++u) {
+      const int it = u * 256 + (int)threadIdx.x;
+      const int rr = it / (HI * 8), rem = it % (HI * 8);
+      const int h = rem >> 3, c8 = rem & 7;
       const int row = rr * HI + h;
       char* dst = qtile + row * kBRow;
+      const v4i v = qpre[u];
       *reinterpret_cast<v8bf*>(dst + (((2 * c8) ^ bswz(h)) << 4)) = widen8(v.x, v.y);
       *reinterpret_cast<v8bf*>(dst + (((2 * c8 + 1) ^ bswz(h)) << 4)) = widen8(v.z, v.w);
     }
-    for (int it = threadIdx.x; it < RPS * kBK; it += 256) {
-      const int rr = it / kBK, kk = it % kBK;
-      const int i = i0 + rr;
-      const int s = s0 + kk;
-      float g = 0.0f;
-      if (i < iend && s <= base + i) g = a.scores[(int64_t)(r0 + i) * a.ld + s];
-      gt[rr][kk] = g;
-    }
-    for (int it = threadIdx.x; it < RPS * HI; it += 256) {
-      const int rr = it / HI, h = it % HI;
-      const int i = min(i0 + rr, iend - 1);
-      const float qs = a.q_scale ? a.q_scale[r0 + i] : 1.0f;
-      wt[rr][h] = a.w[(int64_t)(r0 + i) * a.H_I + h] * qs;
-    }
+    if ((int)threadIdx.x < RPS * kBK) gt[threadIdx.x / kBK][threadIdx.x % kBK] = gpre;
+    if ((int)threadIdx.x < RPS * HI) wt[threadIdx.x / HI][threadIdx.x % HI] = wpre;
     lds_barrier();
+    if (i0 + RPS < iend) load_step(i0 + RPS);
     if (i0 + ro >= iend) continue;              // this wave's row is past the chunk (uniform per wave)
 
     // z[ht][mt]: heads 16*ht + 4*grp + i of the pair, key 16*mt + nl
