@@ -178,12 +178,37 @@ dsa_status dsa_prefill(const dsa_batch* batch, const uint8_t* q8, const float* q
                        void* workspace, size_t ws_bytes, void* stream);
 
 /*
+ * dsa_prefill_streaming — dsa_prefill without the [num_rows, max_len] score
+ * matrix: the top-k selection streams out of the indexer (sider.ai "Sparse
+ * attention that isn't sparse thinking", section "Matematik, Minimalist
+ * Sürüm": selection that stays cache-aware).  Per row, a threshold on the
+ * order (score desc, token asc) is taken from the scores of every 16th token;
+ * the indexer then keeps only the (score, token) pairs at or above it, and the
+ * exact top-k is selected among those.  A row left with fewer than k such
+ * pairs, or more than the candidate capacity, is recomputed exactly (slower,
+ * same result).  The selection, and therefore out/lse/idx_out, equals
+ * dsa_prefill's bit for bit.  Arguments and errors as dsa_prefill, plus
+ * DSA_ERR_UNSUPPORTED unless d_I = 128, k <= 2048 and max_len <= 262144.
+ * Workspace: dsa_workspace_size(DSA_WS_PREFILL_STREAM, ...) bytes, 256-byte
+ * aligned: O(num_rows * (max_len / 16 + 32 * rank)) with rank = max(64,
+ * ceil(7k/64)), instead of num_rows * max_len scores.  Stage events as
+ * dsa_prefill (the indexer stage covers the sampled and the filtered pass).
+ */
+dsa_status dsa_prefill_streaming(const dsa_batch* batch, const uint8_t* q8, const float* q_scale,
+                                 const float* w, const dsa_cache* kidx, const dsa_cache* kscale,
+                                 int H_I, int d_I, int k, const uint16_t* q, const dsa_cache* kv,
+                                 const dsa_cache* v, int H, int D, int D_v, float scale,
+                                 uint16_t* out, float* lse, int32_t* idx_out,
+                                 void* workspace, size_t ws_bytes, void* stream);
+
+/*
  * dsa_set_stage_events — opt-in stage timing for the NEXT dsa_decode,
- * dsa_prefill or dsa_indexer_warmup call on this thread (for profiling
+ * dsa_prefill, dsa_prefill_streaming or dsa_indexer_warmup call on this
+ * thread (for profiling
  * tools; the stages are the ones the pages name: indexer, selection, core
  * attention).  `events` holds `count` >= 4 hipEvent_t handles created by the
  * caller (at most 6 are used); that call records them on its stream:
- *   dsa_decode / dsa_prefill (4 events):
+ *   dsa_decode / dsa_prefill / dsa_prefill_streaming (4 events):
  *     events[0] before the indexer (after the workspace clear),
  *     events[1] after the indexer, events[2] after the top-k,
  *     events[3] after the attention (and its split combine);
@@ -233,11 +258,13 @@ dsa_status dsa_indexer_warmup(const dsa_batch* batch, const uint16_t* q, const d
                               void* workspace, size_t ws_bytes, void* stream);
 
 /* Which call dsa_workspace_size() sizes. */
-enum { DSA_WS_TOPK = 1, DSA_WS_ATTN = 2, DSA_WS_DECODE = 3, DSA_WS_PREFILL = 4, DSA_WS_WARMUP = 5 };
+enum { DSA_WS_TOPK = 1, DSA_WS_ATTN = 2, DSA_WS_DECODE = 3, DSA_WS_PREFILL = 4, DSA_WS_WARMUP = 5,
+       DSA_WS_PREFILL_STREAM = 6 };
 
 /*
  * Workspace bytes `entry` needs for this batch (host-only; no device call).
- * H and D_v matter for DSA_WS_ATTN / DSA_WS_DECODE / DSA_WS_PREFILL only;
+ * H and D_v matter for DSA_WS_ATTN / DSA_WS_DECODE / DSA_WS_PREFILL /
+ * DSA_WS_PREFILL_STREAM only (the last also needs k <= 2048);
  * DSA_WS_WARMUP takes H (the dense heads) and ignores k and D_v.  Returns 0 when the
  * call needs none, and (size_t)-1 for invalid arguments.
  */

@@ -22,11 +22,11 @@ from typing import Optional
 import torch
 
 from . import _lib
-from ._lib import (DSA_WS_ATTN, DSA_WS_DECODE, DSA_WS_PREFILL, DSA_WS_TOPK, DSA_WS_WARMUP,  # noqa: F401
-                   DsaBatch, DsaCache)
+from ._lib import (DSA_WS_ATTN, DSA_WS_DECODE, DSA_WS_PREFILL, DSA_WS_PREFILL_STREAM,  # noqa: F401
+                   DSA_WS_TOPK, DSA_WS_WARMUP, DsaBatch, DsaCache)
 
-__all__ = ["Batch", "DsaError", "indexer", "topk", "sparse_attn", "decode", "prefill", "indexer_warmup",
-           "workspace_size", "cache_view"]
+__all__ = ["Batch", "DsaError", "indexer", "topk", "sparse_attn", "decode", "prefill", "prefill_streaming",
+           "indexer_warmup", "workspace_size", "cache_view"]
 
 
 class DsaError(RuntimeError):
@@ -202,6 +202,14 @@ def prefill(batch: Batch, q8, q_scale, w, k8, k_scale, k: int, q, kv, v, scale: 
     """Whole path for query rows per sequence (dsa_prefill); returns (out, lse, idx_out)."""
     return _fused("dsa_prefill", DSA_WS_PREFILL, batch, q8, q_scale, w, k8, k_scale, k, q, kv, v, scale,
                   out, lse, idx_out, workspace, D_v)
+
+
+def prefill_streaming(batch: Batch, q8, q_scale, w, k8, k_scale, k: int, q, kv, v, scale: float,
+                      out=None, lse=None, idx_out=None, workspace=None, D_v: Optional[int] = None):
+    """dsa_prefill without the score matrix: the selection streams out of the indexer
+    (dsa_prefill_streaming); returns (out, lse, idx_out), equal to prefill's."""
+    return _fused("dsa_prefill_streaming", DSA_WS_PREFILL_STREAM, batch, q8, q_scale, w, k8, k_scale, k, q, kv, v,
+                  scale, out, lse, idx_out, workspace, D_v)
 
 
 def indexer_warmup(batch: Batch, q, kv, scale: float, q8, q_scale, w, k8, k_scale, grads: bool = True,

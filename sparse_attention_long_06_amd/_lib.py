@@ -10,7 +10,7 @@ LIB_PATH = os.path.join(HERE, "libdsa.so")
 DSA_OK, DSA_ERR_NULL, DSA_ERR_SHAPE, DSA_ERR_UNSUPPORTED, DSA_ERR_ALIGN, DSA_ERR_WORKSPACE, DSA_ERR_HIP = range(7)
 STATUS_NAMES = ["DSA_OK", "DSA_ERR_NULL", "DSA_ERR_SHAPE", "DSA_ERR_UNSUPPORTED", "DSA_ERR_ALIGN",
                 "DSA_ERR_WORKSPACE", "DSA_ERR_HIP"]
-DSA_WS_TOPK, DSA_WS_ATTN, DSA_WS_DECODE, DSA_WS_PREFILL, DSA_WS_WARMUP = 1, 2, 3, 4, 5
+DSA_WS_TOPK, DSA_WS_ATTN, DSA_WS_DECODE, DSA_WS_PREFILL, DSA_WS_WARMUP, DSA_WS_PREFILL_STREAM = 1, 2, 3, 4, 5, 6
 
 
 class DsaCache(ctypes.Structure):
@@ -39,6 +39,8 @@ SIGNATURES = {
                    _I),
     "dsa_prefill": ([_BP, _P, _P, _P, _CP, _CP, _I, _I, _I, _P, _CP, _CP, _I, _I, _I, _F, _P, _P, _P, _P, _SZ, _P],
                     _I),
+    "dsa_prefill_streaming": ([_BP, _P, _P, _P, _CP, _CP, _I, _I, _I, _P, _CP, _CP, _I, _I, _I, _F, _P, _P, _P, _P,
+                               _SZ, _P], _I),
     "dsa_indexer_warmup": ([_BP, _P, _CP, _I, _I, _F, _P, _P, _P, _CP, _CP, _I, _I, _P, _P, _P, _P, _P, _SZ, _P],
                            _I),
     "dsa_workspace_size": ([_I, _BP, _I, _I, _I], _SZ),

@@ -197,6 +197,49 @@ FusedPlan plan_fused(int T, int max_len, int k, int H, int D_v) {
   return p;
 }
 
+// Workspace of dsa_prefill_streaming: the compacted sampled keys, the sampled
+// score matrix [T, ceil(max_len / 16)], per-row thresholds and list headers,
+// the candidate lists [T, cap] and their segment records; no [T, max_len]
+// score matrix.
+struct StreamPlan {
+  bool dense = false;
+  int umax = 0, cap = 0, rank = 0;
+  int64_t ld_samp = 0;
+  AttnPlan at;
+  size_t off_keys = 0, off_scale = 0, off_samp = 0, off_thr = 0, off_info = 0, off_redo = 0, off_cnt = 0,
+         off_lists = 0, off_segs = 0, off_idx = 0, off_attn = 0, bytes = 0;
+};
+
+StreamPlan plan_stream(int B, int T, int max_len, int k, int H, int D_v) {
+  StreamPlan p;
+  p.dense = max_len <= k;
+  p.at = plan_attn(T, k, H, D_v);
+  size_t o = 0;
+  auto take = [&](size_t& off, size_t n) {
+    off = o;
+    o = (size_t)round_up((int64_t)(o + n), 256);
+  };
+  if (!p.dense) {
+    p.umax = (max_len + kStreamStride - 1) / kStreamStride;
+    p.ld_samp = round_up(p.umax, 4);
+    p.cap = stream_cap(k);
+    p.rank = stream_rank(k);
+    take(p.off_keys, (size_t)B * p.umax * 128);
+    take(p.off_scale, (size_t)B * p.umax * 4);
+    take(p.off_samp, (size_t)T * p.ld_samp * 4);
+    take(p.off_thr, (size_t)T * 8);
+    take(p.off_info, (size_t)T * 8);
+    take(p.off_redo, (size_t)T * 4);
+    take(p.off_cnt, 4);
+    take(p.off_lists, (size_t)T * p.cap * 8);
+    take(p.off_segs, (size_t)T * kStreamMaxSegs * 8);
+  }
+  take(p.off_idx, (size_t)T * k * 4);
+  take(p.off_attn, p.at.bytes);
+  p.bytes = o;
+  return p;
+}
+
 // Workspace of dsa_indexer_warmup: the [T, ld] score matrix (overwritten by
 // dI), the per-head dense log-sum-exps and the per-chunk key-gradient partials.
 struct WarmPlan {
@@ -397,6 +440,9 @@ extern "C" size_t dsa_workspace_size(int entry, const dsa_batch* batch, int k, i
     case DSA_WS_PREFILL:
       if (H < 1 || D_v < 1 || !batch->q_start) return (size_t)-1;
       return plan_fused(batch->num_rows, batch->max_len, k, H, D_v).bytes;
+    case DSA_WS_PREFILL_STREAM:
+      if (H < 1 || D_v < 1 || !batch->q_start || k > kStreamMaxK) return (size_t)-1;
+      return plan_stream(batch->num_seqs, batch->num_rows, batch->max_len, k, H, D_v).bytes;
     default:
       return (size_t)-1;
   }
@@ -497,20 +543,120 @@ dsa_status run_fused(const dsa_batch* batch, const uint8_t* q8, const float* q_s
   return DSA_OK;
 }
 
-dsa_status check_fused(const dsa_batch* batch, const uint8_t* q8, const float* w, const dsa_cache* kidx,
-                       const dsa_cache* kscale, int H_I, int d_I, int k, const uint16_t* q, const dsa_cache* kv,
-                       const dsa_cache* v, int H, int D, int D_v, float scale, uint16_t* out, const FusedPlan& p,
-                       void* workspace, size_t ws_bytes) {
+dsa_status check_fused_bytes(const dsa_batch* batch, const uint8_t* q8, const float* w, const dsa_cache* kidx,
+                             const dsa_cache* kscale, int H_I, int d_I, int k, const uint16_t* q,
+                             const dsa_cache* kv, const dsa_cache* v, int H, int D, int D_v, float scale,
+                             uint16_t* out, size_t need, void* workspace, size_t ws_bytes) {
   dsa_status st = check_indexer_args(batch, q8, w, kidx, kscale, H_I, d_I);
   if (st != DSA_OK) return st;
   st = check_attn_args(batch, q, kv, v, H, D, D_v, scale, k);
   if (st != DSA_OK) return st;
   CHECK(out, DSA_ERR_NULL, "out is NULL");
-  CHECK(workspace, DSA_ERR_WORKSPACE, "the fused path needs %zu workspace bytes, got NULL", p.bytes);
-  CHECK(ws_bytes >= p.bytes, DSA_ERR_WORKSPACE, "the fused path needs %zu workspace bytes, got %zu", p.bytes,
-        ws_bytes);
+  CHECK(workspace, DSA_ERR_WORKSPACE, "the fused path needs %zu workspace bytes, got NULL", need);
+  CHECK(ws_bytes >= need, DSA_ERR_WORKSPACE, "the fused path needs %zu workspace bytes, got %zu", need, ws_bytes);
   CHECK(aligned(workspace, 256), DSA_ERR_ALIGN, "workspace not 256-byte aligned");
   return DSA_OK;
+}
+
+// The streaming prefill path (dsa_prefill_streaming), enqueued on one stream:
+// sampled keys -> sampled scores -> row thresholds -> filtered indexer ->
+// finalize (+ recompute of the rows it lists) -> attention.
+dsa_status run_stream(const dsa_batch* batch, const uint8_t* q8, const float* q_scale, const float* w,
+                      const dsa_cache* kidx, const dsa_cache* kscale, int H_I, int k, const uint16_t* q,
+                      const dsa_cache* kv, const dsa_cache* v, int H, int D, int D_v, float scale, uint16_t* out,
+                      float* lse, int32_t* idx_out, const StreamPlan& p, char* ws, hipStream_t s) {
+  int32_t* idx = idx_out ? idx_out : reinterpret_cast<int32_t*>(ws + p.off_idx);
+  const bool timed = g_stage_armed;
+  g_stage_armed = false;
+  auto mark = [&](int i) -> hipError_t { return timed ? hipEventRecord(g_stage_events[i], s) : hipSuccess; };
+  StreamArgs sa;
+  sa.g = make_geo(batch);
+  sa.kidx = make_cache(kidx);
+  sa.ksc = make_cache((kscale && kscale->data) ? kscale : nullptr);
+  sa.q8 = q8;
+  sa.q_scale = q_scale;
+  sa.w = w;
+  sa.H_I = H_I;
+  sa.k = k;
+  sa.cap = p.cap;
+  sa.rank = p.rank;
+  sa.umax = p.umax;
+  sa.samp_keys = ws + p.off_keys;
+  sa.samp_scale = reinterpret_cast<float*>(ws + p.off_scale);
+  sa.samp = reinterpret_cast<const float*>(ws + p.off_samp);
+  sa.ld_samp = p.ld_samp;
+  sa.thr = reinterpret_cast<unsigned long long*>(ws + p.off_thr);
+  sa.rowinfo = reinterpret_cast<unsigned long long*>(ws + p.off_info);
+  sa.lists = reinterpret_cast<const uint2*>(ws + p.off_lists);
+  sa.segs = reinterpret_cast<const uint2*>(ws + p.off_segs);
+  sa.redo = reinterpret_cast<int*>(ws + p.off_redo);
+  sa.redo_count = reinterpret_cast<uint32_t*>(ws + p.off_cnt);
+  sa.idx = idx;
+  LAUNCH(mark(0), "stage event");
+  if (!p.dense) {
+    LAUNCH(launch_stream_gather(sa, s), "sampled-key gather launch");
+    // the prefill indexer over the compacted sampled keys (key u = token 16u)
+    IndexerArgs ia;
+    ia.g = sa.g;
+    ia.g.block_table = nullptr;
+    ia.g.block_shift = 0;
+    ia.kidx = Cache{sa.samp_keys, 128, p.umax};
+    ia.ksc = sa.ksc.data ? Cache{reinterpret_cast<const char*>(sa.samp_scale), 4, p.umax} : Cache{nullptr, 0, 0};
+    ia.q8 = q8;
+    ia.q_scale = q_scale;
+    ia.w = w;
+    ia.scores = reinterpret_cast<float*>(ws + p.off_samp);
+    ia.ld = p.ld_samp;
+    ia.hist = nullptr;
+    ia.H_I = H_I;
+    ia.chunk = kIdxPrefillChunk;
+    ia.ntiles = (batch->max_q + kIdxPrefillRows - 1) / kIdxPrefillRows;
+    ia.nchunks = (p.umax + ia.chunk - 1) / ia.chunk;
+    ia.kshift = kStreamShift;
+    LAUNCH(launch_indexer(ia, 128, false, false, s), "sampled indexer launch");
+    LAUNCH(launch_stream_threshold(sa, s), "threshold launch");
+    IndexerArgs fa;
+    fa.g = sa.g;
+    fa.kidx = sa.kidx;
+    fa.ksc = sa.ksc;
+    fa.q8 = q8;
+    fa.q_scale = q_scale;
+    fa.w = w;
+    fa.scores = nullptr;
+    fa.ld = 0;
+    fa.hist = nullptr;
+    fa.H_I = H_I;
+    fa.chunk = kIdxPrefillChunk;
+    fa.ntiles = ia.ntiles;
+    fa.nchunks = (batch->max_len + fa.chunk - 1) / fa.chunk;
+    fa.thr = sa.thr;
+    fa.rowinfo = sa.rowinfo;
+    fa.lists = reinterpret_cast<uint2*>(ws + p.off_lists);
+    fa.segs = reinterpret_cast<uint2*>(ws + p.off_segs);
+    fa.cap = p.cap;
+    CHECK((int64_t)fa.nchunks * fa.ntiles < (int64_t)1 << 31, DSA_ERR_UNSUPPORTED, "indexer grid too large");
+    LAUNCH(launch_indexer_stream(fa, s), "filtered indexer launch");
+  }
+  LAUNCH(mark(1), "stage event");
+  if (p.dense) {
+    dsa_status st = run_topk(batch, nullptr, 4, k, idx, TopkPlan{}, nullptr, false, s);
+    if (st != DSA_OK) return st;
+  } else {
+    LAUNCH(launch_stream_finalize(sa, s), "streaming finalize launch");
+  }
+  LAUNCH(mark(2), "stage event");
+  dsa_status st = run_attn(batch, q, kv, v, H, D, D_v, scale, idx, k, out, lse, p.at, ws + p.off_attn, s);
+  if (st != DSA_OK) return st;
+  LAUNCH(mark(3), "stage event");
+  return DSA_OK;
+}
+
+dsa_status check_fused(const dsa_batch* batch, const uint8_t* q8, const float* w, const dsa_cache* kidx,
+                       const dsa_cache* kscale, int H_I, int d_I, int k, const uint16_t* q, const dsa_cache* kv,
+                       const dsa_cache* v, int H, int D, int D_v, float scale, uint16_t* out, const FusedPlan& p,
+                       void* workspace, size_t ws_bytes) {
+  return check_fused_bytes(batch, q8, w, kidx, kscale, H_I, d_I, k, q, kv, v, H, D, D_v, scale, out, p.bytes,
+                           workspace, ws_bytes);
 }
 
 }  // namespace
@@ -546,6 +692,31 @@ extern "C" dsa_status dsa_prefill(const dsa_batch* batch, const uint8_t* q8, con
   if (batch->num_rows == 0) return ok();
   st = run_fused(batch, q8, q_scale, w, kidx, kscale, H_I, d_I, k, q, kv, v, H, D, D_v, scale, out, lse, idx_out, p,
                  static_cast<char*>(workspace), static_cast<hipStream_t>(stream));
+  return st == DSA_OK ? ok() : st;
+}
+
+extern "C" dsa_status dsa_prefill_streaming(const dsa_batch* batch, const uint8_t* q8, const float* q_scale,
+                                            const float* w, const dsa_cache* kidx, const dsa_cache* kscale, int H_I,
+                                            int d_I, int k, const uint16_t* q, const dsa_cache* kv,
+                                            const dsa_cache* v, int H, int D, int D_v, float scale, uint16_t* out,
+                                            float* lse, int32_t* idx_out, void* workspace, size_t ws_bytes,
+                                            void* stream) {
+  dsa_status st = check_batch(batch);
+  if (st != DSA_OK) return st;
+  CHECK(batch->q_start != nullptr, DSA_ERR_SHAPE,
+        "dsa_prefill_streaming takes query rows per sequence (q_start must be set)");
+  CHECK(d_I == 128, DSA_ERR_UNSUPPORTED, "dsa_prefill_streaming supports d_I = 128 (got %d)", d_I);
+  CHECK(k >= 1 && k <= kStreamMaxK, DSA_ERR_UNSUPPORTED, "dsa_prefill_streaming supports k in [1, %d] (got %d)",
+        kStreamMaxK, k);
+  CHECK(batch->max_len <= kStreamMaxLen, DSA_ERR_UNSUPPORTED, "dsa_prefill_streaming supports max_len <= %d (got %d)",
+        kStreamMaxLen, batch->max_len);
+  const StreamPlan p = plan_stream(batch->num_seqs, batch->num_rows, batch->max_len, k, H, D_v);
+  st = check_fused_bytes(batch, q8, w, kidx, kscale, H_I, d_I, k, q, kv, v, H, D, D_v, scale, out, p.bytes,
+                         workspace, ws_bytes);
+  if (st != DSA_OK) return st;
+  if (batch->num_rows == 0) return ok();
+  st = run_stream(batch, q8, q_scale, w, kidx, kscale, H_I, k, q, kv, v, H, D, D_v, scale, out, lse, idx_out, p,
+                  static_cast<char*>(workspace), static_cast<hipStream_t>(stream));
   return st == DSA_OK ? ok() : st;
 }
 

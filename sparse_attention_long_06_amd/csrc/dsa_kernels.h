@@ -23,6 +23,18 @@ struct IndexerArgs {
   int chunk;             // keys per workgroup
   int nchunks;           // key chunks per row tile
   int ntiles;            // row tiles per sequence
+  // Prefill layout only.  kshift > 0: key u of the cache stands for token
+  // u << kshift (a compacted sample of every 2^kshift-th token), so row t sees
+  // keys u <= p_t >> kshift.
+  int kshift = 0;
+  // Streaming selection (filtered epilogue): scores are not stored; the pairs
+  // (key, token) whose order (key desc, token asc) reaches the row threshold
+  // go to per-row candidate lists in segments (see launch_indexer_stream).
+  const unsigned long long* thr = nullptr;   // [T] (key << 32) | ~token of the row threshold
+  unsigned long long* rowinfo = nullptr;     // [T] low 32: candidates reserved, high 32: segments
+  uint2* lists = nullptr;                    // [T, cap] (key, token)
+  uint2* segs = nullptr;                     // [T, kStreamMaxSegs] (chunk << 3 | flush, base << 16 | count)
+  int cap = 0;
 };
 
 // Rows of one workgroup in the prefill layout (4 waves x kIdxRowsPerWave rows).
@@ -33,6 +45,53 @@ constexpr int kIdxDecodeChunk = 2048;
 
 hipError_t launch_indexer(const IndexerArgs& a, int d_I, bool decode_layout, bool with_hist,
                           hipStream_t stream);
+
+// ---------------------------------------------------------------- streaming prefill selection
+// The threshold of a row comes from the scores of every kStreamStride-th
+// token; the filtered indexer keeps the pairs at or above it in LDS buffers of
+// kStreamLds entries per (wave, row) and flushes them as segments.
+constexpr int kStreamShift = 4;
+constexpr int kStreamStride = 1 << kStreamShift;
+constexpr int kStreamLds = 448;
+constexpr int kStreamMaxSegs = 512;
+constexpr int kStreamMaxK = 2048;
+constexpr int kStreamMaxLen = 262144;
+
+// Rank of the threshold among a row's sampled scores, and the candidate
+// capacity per row (twice the expected count kStreamStride * rank).
+__host__ __device__ constexpr int stream_rank(int k) { return (7 * k + 63) / 64 > 64 ? (7 * k + 63) / 64 : 64; }
+__host__ __device__ constexpr int stream_cap(int k) { return 2 * kStreamStride * stream_rank(k); }
+
+hipError_t launch_indexer_stream(const IndexerArgs& a, hipStream_t stream);
+
+struct StreamArgs {
+  Geo g;
+  Cache kidx;            // 128 FP8 bytes per token
+  Cache ksc;             // fp32 per token; data == nullptr means 1
+  const uint8_t* q8;     // [T, H_I, 128]
+  const float* q_scale;  // [T] or nullptr
+  const float* w;        // [T, H_I]
+  int H_I;
+  int k;
+  int cap;               // stream_cap(k)
+  int rank;              // stream_rank(k)
+  int umax;              // sampled keys per sequence: ceil(max_len / kStreamStride)
+  char* samp_keys;       // [B, umax, 128] compacted sampled keys
+  float* samp_scale;     // [B, umax] their scales (when ksc.data)
+  const float* samp;     // [T, ld_samp] sampled scores
+  int64_t ld_samp;
+  unsigned long long* thr;
+  unsigned long long* rowinfo;
+  const uint2* lists;
+  const uint2* segs;
+  int* redo;             // [T] rows the finalize leaves to the fallback
+  uint32_t* redo_count;
+  int32_t* idx;          // [T, k]
+};
+
+hipError_t launch_stream_gather(const StreamArgs& a, hipStream_t stream);
+hipError_t launch_stream_threshold(const StreamArgs& a, hipStream_t stream);
+hipError_t launch_stream_finalize(const StreamArgs& a, hipStream_t stream);
 
 // ---------------------------------------------------------------- top-k
 struct TopkArgs {

@@ -35,89 +35,9 @@
 //           position are skipped (causality).
 #include "dsa_common.h"
 #include "dsa_kernels.h"
+#include "idx_math.h"
 
 namespace dsa {
-
-// Raw FP8 fragment of one row held by a lane: d_I/4 bytes.
-template <int DI> struct Frag;
-template <> struct Frag<128> { v4i lo, hi; };
-template <> struct Frag<32> { long v; };
-
-template <int DI, bool NT>
-__device__ __forceinline__ void load_frag(Frag<DI>& f, const char* row, int grp) {
-  if constexpr (DI == 128) {
-    const v4i* p = reinterpret_cast<const v4i*>(row + 32 * grp);
-    if constexpr (NT) {
-      f.lo = __builtin_nontemporal_load(p);
-      f.hi = __builtin_nontemporal_load(p + 1);
-    } else {
-      f.lo = p[0];
-      f.hi = p[1];
-    }
-  } else {
-    const long* p = reinterpret_cast<const long*>(row + 8 * grp);
-    if constexpr (NT) f.v = __builtin_nontemporal_load(p); else f.v = *p;
-  }
-}
-
-template <int DI>
-__device__ __forceinline__ void zero_frag(Frag<DI>& f) {
-  if constexpr (DI == 128) {
-    f.lo = v4i{0, 0, 0, 0};
-    f.hi = v4i{0, 0, 0, 0};
-  } else {
-    f.v = 0;
-  }
-}
-
-typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
-
-// Eight e4m3fn bytes (two dwords) -> eight bf16, exactly.
-__device__ __forceinline__ v8bf widen8(int lo, int hi) {
-  const v2bf a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false);
-  const v2bf b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true);
-  const v2bf c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false);
-  const v2bf d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true);
-  return v8bf{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
-}
-
-// bf16 view of a fragment: d_I/32 chunks of 8 values.
-template <int DI> struct Wide { v8bf c[DI / 32]; };
-
-template <int DI>
-__device__ __forceinline__ Wide<DI> widen(const Frag<DI>& f) {
-  Wide<DI> w;
-  if constexpr (DI == 128) {
-    w.c[0] = widen8(f.lo.x, f.lo.y);
-    w.c[1] = widen8(f.lo.z, f.lo.w);
-    w.c[2] = widen8(f.hi.x, f.hi.y);
-    w.c[3] = widen8(f.hi.z, f.hi.w);
-  } else {
-    w.c[0] = widen8((int)(f.v & 0xFFFFFFFF), (int)(f.v >> 32));
-  }
-  return w;
-}
-
-template <int DI>
-__device__ __forceinline__ v4f mfma_dot(const Wide<DI>& a, const Wide<DI>& b) {
-  v4f acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int c = 0; c < DI / 32; ++c) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.c[c], b.c[c], acc, 0, 0, 0);
-  return acc;
-}
-
-// ReLU of a finite MFMA result as a clamp to [0, FLT_MAX]: one v_med3_f32,
-// where fmaxf would add a NaN-quieting canonicalize.
-__device__ __forceinline__ float relu(float x) { return __builtin_amdgcn_fmed3f(x, 0.0f, 3.402823466e38f); }
-
-// Sum over the four 16-lane groups (rows) of a wave: after the row swaps every
-// lane holds the total of its column.  Pure VALU (no LDS permute).
-__device__ __forceinline__ float group_sum(float part) {
-  const auto r16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(part), __float_as_uint(part), false, false);
-  part = __uint_as_float(r16[0]) + __uint_as_float(r16[1]);
-  const auto r32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(part), __float_as_uint(part), false, false);
-  return __uint_as_float(r32[0]) + __uint_as_float(r32[1]);
-}
 
 template <int HT, int DI, int R, int RW, bool HIST>
 __global__ void __launch_bounds__(256) indexer_kernel(IndexerArgs a) {
@@ -492,14 +412,16 @@ __global__ void __launch_bounds__(256) indexer_decode_ring_kernel(IndexerArgs a)
 constexpr int kPreRing = 6;
 constexpr int kPreKeys = 64;
 
-template <int HT, bool SCALE>
+template <int HT, bool SCALE, bool FILT>
 __global__ void __launch_bounds__(256) indexer_prefill_ring_kernel(IndexerArgs a) {
   constexpr int DI = 128;
   constexpr int R = 2;                                // rows per wave
   constexpr int SLOT = kPreKeys * DI + kPreKeys * 4;  // keys + scales
   constexpr int PER = SCALE ? 3 : 2;                  // DMA instructions per wave per slot
-  constexpr int ST = R * (kPreKeys / 16);             // score stores per wave per slot
+  constexpr int ST = FILT ? 0 : R * (kPreKeys / 16);  // score stores per wave per slot
   __shared__ __attribute__((aligned(16))) char ring[kPreRing][SLOT];
+  // FILT: this wave's candidate buffers, one per row (kStreamLds pairs each)
+  __shared__ uint2 cand[FILT ? 4 * R * kStreamLds : 1];
 
   const int b = blockIdx.z;
   const int ytile = blockIdx.x % a.ntiles;
@@ -516,7 +438,7 @@ __global__ void __launch_bounds__(256) indexer_prefill_ring_kernel(IndexerArgs a
   const int base_pos = len - nq;
   const int last_r = min(tile_r0 + 4 * R, nq) - 1;
   const int kbeg = chunk_id * a.chunk;
-  const int kend = min(kbeg + a.chunk, base_pos + last_r + 1);
+  const int kend = min(kbeg + a.chunk, ((base_pos + last_r) >> a.kshift) + 1);
   if (kbeg >= kend) return;                           // uniform over the workgroup
   const int nslots = (kend - kbeg + kPreKeys - 1) / kPreKeys;
   // a partial row tile stores fewer scores per slot: it waits for everything
@@ -619,6 +541,43 @@ __global__ void __launch_bounds__(256) indexer_prefill_ring_kernel(IndexerArgs a
       wq[r][ht][3] = w4.w * qs;
     }
   }
+  // FILT: per row its position (-1: no row), threshold, buffered pairs and
+  // the number of segments this workgroup has flushed for it (all uniform)
+  int rpos[R];
+  unsigned long long rthr[R];
+  uint32_t ccnt[R], cfl[R];
+  if constexpr (FILT) {
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int ri = tile_r0 + wave * R + r;
+      rpos[r] = ri < nq ? base_pos + ri : -1;
+      rthr[r] = ri < nq ? a.thr[row0 + ri] : ~0ull;
+      ccnt[r] = 0u;
+      cfl[r] = 0u;
+    }
+  }
+  uint2* const mycand = &cand[FILT ? wave * R * kStreamLds : 0];
+  // Move row r's buffered pairs to its list: one 64-bit atomic reserves the
+  // space and the segment number, then the pairs and the segment record
+  // (chunk, flush number, base, count) are stored.  Pairs past the row's
+  // capacity are dropped; the finalize sees the total and recomputes the row.
+  auto flush = [&](int r) {
+    const uint32_t c = ccnt[r];
+    if (c == 0u) return;
+    const int64_t t = trow[r];
+    unsigned long long old = 0ull;
+    if (lane == 0) old = atomicAdd(&a.rowinfo[t], (1ull << 32) | (unsigned long long)c);
+    const uint32_t base = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)old);
+    const uint32_t seg = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(old >> 32));
+    const uint2* src = mycand + r * kStreamLds;
+    uint2* dst = a.lists + t * a.cap;
+    for (uint32_t i = lane; i < c; i += 64)
+      if (base + i < (uint32_t)a.cap) dst[base + i] = src[i];
+    if (lane == 0 && seg < (uint32_t)kStreamMaxSegs)
+      a.segs[t * kStreamMaxSegs + seg] = make_uint2(((uint32_t)chunk_id << 3) | cfl[r], (base << 16) | c);
+    ccnt[r] = 0u;
+    cfl[r] += 1u;
+  };
   __builtin_amdgcn_s_waitcnt(0x0F70);                 // rows and ring prologue are in
 
   const int rb0 = nl * DI + 16 * ((2 * grp) ^ kswz(nl));
@@ -660,9 +619,31 @@ __global__ void __launch_bounds__(256) indexer_prefill_ring_kernel(IndexerArgs a
           for (int i = 0; i < 4; ++i) part = fmaf(wq[r][ht][i], relu(acc[i]), part);
         }
         part = group_sum(part);
-        if (grp == 0 && s < kend && trow[r] >= 0) a.scores[trow[r] * a.ld + s] = part * ks;
+        if constexpr (FILT) {
+          // keep (key, token) when s <= p and (key, ~s) reaches the threshold;
+          // lanes 0-15 hold keys 16j .. 16j+15 of the slot in order, so the
+          // buffer (and each segment) stays in token order
+          const uint32_t key = score_key(part * ks);
+          const unsigned long long comp = ((unsigned long long)key << 32) | (uint32_t)~(uint32_t)s;
+          const bool keep = grp == 0 && s <= rpos[r] && comp >= rthr[r];
+          const unsigned long long m64 = __ballot(keep);
+          if (m64) {                                  // uniform
+            const uint32_t c = (uint32_t)__popcll(m64);
+            if (ccnt[r] + c > (uint32_t)kStreamLds) flush(r);
+            const uint32_t before = __builtin_amdgcn_mbcnt_hi((uint32_t)(m64 >> 32),
+                                                              __builtin_amdgcn_mbcnt_lo((uint32_t)m64, 0u));
+            if (keep) mycand[r * kStreamLds + ccnt[r] + before] = make_uint2(key, (uint32_t)s);
+            ccnt[r] += c;
+          }
+        } else {
+          if (grp == 0 && s < kend && trow[r] >= 0) a.scores[trow[r] * a.ld + s] = part * ks;
+        }
       }
     }
+  }
+  if constexpr (FILT) {
+#pragma unroll
+    for (int r = 0; r < R; ++r) flush(r);
   }
 }
 
@@ -684,8 +665,8 @@ static hipError_t launch_ht(const IndexerArgs& a, bool decode_layout, bool with_
     else
       hipLaunchKernelGGL((indexer_kernel<HT, DI, 1, 1, false>), grid, dim3(256), 0, s, a);
   } else if (DI == 128) {
-    if (a.ksc.data) hipLaunchKernelGGL((indexer_prefill_ring_kernel<HT, true>), grid, dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((indexer_prefill_ring_kernel<HT, false>), grid, dim3(256), 0, s, a);
+    if (a.ksc.data) hipLaunchKernelGGL((indexer_prefill_ring_kernel<HT, true, false>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((indexer_prefill_ring_kernel<HT, false, false>), grid, dim3(256), 0, s, a);
   } else {
     hipLaunchKernelGGL((indexer_kernel<HT, DI, kIdxRowsPerWave, 4, false>), grid, dim3(256), 0, s, a);
   }
@@ -699,6 +680,26 @@ static hipError_t launch_di(const IndexerArgs& a, bool decode_layout, bool with_
     case 2: return launch_ht<2, DI>(a, decode_layout, with_hist, s);
     case 3: return launch_ht<3, DI>(a, decode_layout, with_hist, s);
     case 4: return launch_ht<4, DI>(a, decode_layout, with_hist, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <int HT>
+static hipError_t launch_stream_ht(const IndexerArgs& a, hipStream_t s) {
+  const dim3 grid(a.nchunks * a.ntiles, 1, a.g.num_seqs);
+  if (a.ksc.data) hipLaunchKernelGGL((indexer_prefill_ring_kernel<HT, true, true>), grid, dim3(256), 0, s, a);
+  else hipLaunchKernelGGL((indexer_prefill_ring_kernel<HT, false, true>), grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+// The prefill layout with the filtered epilogue (d_I = 128): rowinfo must be
+// zero and thr set for every row before the launch.
+hipError_t launch_indexer_stream(const IndexerArgs& a, hipStream_t stream) {
+  switch ((a.H_I + 15) / 16) {
+    case 1: return launch_stream_ht<1>(a, stream);
+    case 2: return launch_stream_ht<2>(a, stream);
+    case 3: return launch_stream_ht<3>(a, stream);
+    case 4: return launch_stream_ht<4>(a, stream);
     default: return hipErrorInvalidValue;
   }
 }

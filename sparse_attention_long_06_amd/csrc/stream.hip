@@ -1,0 +1,328 @@
+// Streaming top-k selection for prefill on gfx950: the lightning indexer's
+// scores are never stored as a [rows, tokens] matrix; only the (key, token)
+// pairs that can still be among a row's top k leave the indexer (sider.ai
+// "Sparse attention that isn't sparse thinking", section "Matematik,
+// Minimalist Sürüm": candidate selection has to stay vectorised and
+// cache-aware, or its memory traffic eats the gain; ouchyi.pink post, DSA
+// paragraph: a fixed budget of k tokens per query).
+//
+// Order: score descending, then token ascending, i.e. the pair order of
+// c(s) = (key(s) << 32) | ~s with key the order-preserving map of the score.
+// The selection is the k largest c(s), s <= p, emitted in ascending s.
+//
+// Launches (stream order is the only synchronisation):
+//   gather     every kStreamStride-th token's index key (and scale) of each
+//              sequence, compacted, so the prefill indexer can score them;
+//   [indexer over the compacted keys: the sampled scores]
+//   threshold  per row, thr = the rank-th largest c over its sampled tokens;
+//              rows with n <= cap take thr = 0 (every token), rows with
+//              n <= k need none;
+//   [filtered indexer: pairs with c >= thr go to segment lists]
+//   finalize   per row, the segments sorted by (chunk, flush) give the
+//              candidates in token order; the same radix select and ordered
+//              compaction as the top-k kernels picks the k largest.
+// Exactness: every token with c >= thr is a candidate.  When at least k are,
+// the k-th largest c is >= thr, so the top k are all among them.  A row with
+// fewer than k candidates, or more than cap (or too many segments), is listed
+// by the finalize and recomputed by a fallback launch: scores in batches,
+// radix passes and ordered compaction over the recomputed batches, nothing
+// stored.
+#include "dsa_common.h"
+#include "dsa_kernels.h"
+#include "idx_math.h"
+#include "select_blocks.h"
+
+namespace dsa {
+
+namespace {
+
+__global__ void __launch_bounds__(256) stream_gather_kernel(StreamArgs a) {
+  const int b = blockIdx.y;
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  const int u = i >> 3, c = i & 7;                       // sampled token, 16-byte chunk of its key
+  const int len = a.g.seq_lens[b];
+  if (u >= (len + kStreamStride - 1) >> kStreamShift) return;
+  const int s = u << kStreamShift;
+  const v4i v = *reinterpret_cast<const v4i*>(token_ptr(a.g, a.kidx, b, s) + 16 * c);
+  *reinterpret_cast<v4i*>(a.samp_keys + ((int64_t)b * a.umax + u) * 128 + 16 * c) = v;
+  if (c == 0 && a.ksc.data)
+    a.samp_scale[(int64_t)b * a.umax + u] = *reinterpret_cast<const float*>(token_ptr(a.g, a.ksc, b, s));
+}
+
+constexpr int kThrNT = 256;
+
+__global__ void __launch_bounds__(kThrNT) stream_threshold_kernel(StreamArgs a) {
+  __shared__ uint32_t hist[kBins1];
+  __shared__ uint32_t tmp[kUnr * kThrNT / 64];
+  __shared__ BinSel res;
+  __shared__ unsigned long long tmin;
+
+  const int t = blockIdx.x;
+  int b, pos;
+  row_seq_pos(a.g, t, b, pos);
+  const int n = pos + 1;
+  if (threadIdx.x == 0) a.rowinfo[t] = 0ull;
+  if (t == 0 && threadIdx.x == 0) *a.redo_count = 0u;
+  unsigned long long thr;
+  if (n <= a.k) {
+    thr = ~0ull;                                         // identity selection: keep nothing
+  } else if (n <= a.cap) {
+    thr = 0ull;                                          // every token is a candidate
+  } else {
+    // the rank-th largest pair order among the sampled tokens u <= p >> shift
+    // (token u << shift); m > 2 * rank because n > cap
+    const int m = (pos >> kStreamShift) + 1;
+    const RowSrc src{a.samp + (int64_t)t * a.ld_samp, m, 0};
+    if (threadIdx.x == 0) tmin = ~0ull;
+    lds_barrier();
+    const uint32_t r = (uint32_t)a.rank;
+    refine_and_emit<kThrNT>(src, 0u, 0, r, (uint32_t)m, hist, tmp, &res, r,
+                            [&](uint32_t, uint32_t key, int id) {
+                              const uint32_t tok = (uint32_t)id << kStreamShift;
+                              atomicMin(&tmin, ((unsigned long long)key << 32) | (uint32_t)~tok);
+                            });
+    lds_barrier();
+    thr = tmin;
+  }
+  if (threadIdx.x == 0) a.thr[t] = thr;
+}
+
+constexpr int kFinNT = 512;
+constexpr int kFinBatch = kFinNT * 4 * kUnr;             // tokens per recomputed batch (fallback)
+// LDS layout of the batch buffer on the candidate path: keys [cap], tokens
+// [cap], then the segment tables
+constexpr int kFinSegOff = 8 * 7168;
+static_assert(stream_cap(kStreamMaxK) <= 7168, "candidate pairs must fit before the segment tables");
+constexpr int kRedoGrid = 256;
+
+// Scores of tokens [base, base + kFinBatch) of row t (those < n) into sc,
+// with the arithmetic of the prefill indexer in the same order, so that they
+// equal the scores the indexer produces bit for bit.
+template <int HT>
+struct RowScorer {
+  Wide<128> qa[HT];
+  float wq[HT][4];
+
+  __device__ void init(const StreamArgs& a, int t, int nl, int grp) {
+    const float qs = a.q_scale ? a.q_scale[t] : 1.0f;
+#pragma unroll
+    for (int ht = 0; ht < HT; ++ht) {
+      const int h = ht * 16 + nl;
+      Frag<128> raw;
+      if (h < a.H_I)
+        load_frag<128, false>(raw, reinterpret_cast<const char*>(a.q8) + ((int64_t)t * a.H_I + h) * 128, grp);
+      else
+        zero_frag<128>(raw);
+      qa[ht] = widen<128>(raw);
+      const int hw = ht * 16 + grp * 4;
+      const float4 w4 = hw < a.H_I ? *reinterpret_cast<const float4*>(a.w + (int64_t)t * a.H_I + hw)
+                                   : make_float4(0.f, 0.f, 0.f, 0.f);
+      wq[ht][0] = w4.x * qs;
+      wq[ht][1] = w4.y * qs;
+      wq[ht][2] = w4.z * qs;
+      wq[ht][3] = w4.w * qs;
+    }
+  }
+
+  __device__ void stage(const StreamArgs& a, int b, int n, int base, float* sc, int wave, int nl, int grp) const {
+    const int nk = min(kFinBatch, n - base);
+    const int ngroups = (nk + 15) / 16;
+    for (int gi = wave; gi < ngroups; gi += kFinNT / 64) {
+      const int s = base + gi * 16 + nl;
+      const int sl = min(s, n - 1);
+      Frag<128> kf;
+      load_frag<128, false>(kf, token_ptr(a.g, a.kidx, b, sl), grp);
+      const float ks = a.ksc.data ? *reinterpret_cast<const float*>(token_ptr(a.g, a.ksc, b, sl)) : 1.0f;
+      const Wide<128> kb = widen<128>(kf);
+      float part = 0.0f;
+#pragma unroll
+      for (int ht = 0; ht < HT; ++ht) {
+        const v4f acc = mfma_dot<128>(qa[ht], kb);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) part = fmaf(wq[ht][i], relu(acc[i]), part);
+      }
+      part = group_sum(part);
+      if (grp == 0 && s < n) sc[gi * 16 + nl] = part * ks;
+    }
+  }
+};
+
+__global__ void __launch_bounds__(kFinNT) __attribute__((amdgpu_waves_per_eu(4)))
+stream_finalize_kernel(StreamArgs a) {
+  __shared__ uint32_t hist[kBins1];
+  __shared__ uint32_t tmp[kUnr * kFinNT / 64];
+  __shared__ BinSel res;
+  __shared__ __attribute__((aligned(16))) char big[kFinSegOff + 16 * kStreamMaxSegs];
+
+  const int t = blockIdx.x;
+  int b, pos;
+  row_seq_pos(a.g, t, b, pos);
+  const int n = pos + 1;
+  const uint32_t k = (uint32_t)a.k;
+  int32_t* out = a.idx + (int64_t)t * a.k;
+  if (n <= a.k) {
+    write_identity(out, n, a.k, threadIdx.x, kFinNT);
+    return;
+  }
+  const unsigned long long info = a.rowinfo[t];
+  const uint32_t total = (uint32_t)info, nseg = (uint32_t)(info >> 32);
+  if (!(total >= k && total <= (uint32_t)a.cap && nseg <= (uint32_t)kStreamMaxSegs)) {
+    if (threadIdx.x == 0) a.redo[atomicAdd(a.redo_count, 1u)] = t;   // recomputed by the fallback launch
+    return;
+  }
+  uint32_t* lkey = reinterpret_cast<uint32_t*>(big);
+  int* lidx = reinterpret_cast<int*>(big + 4 * a.cap);
+  uint32_t* skey = reinterpret_cast<uint32_t*>(big + kFinSegOff);
+  uint32_t* sinfo = skey + kStreamMaxSegs;
+  uint32_t* soff = sinfo + kStreamMaxSegs;
+  int* sorder = reinterpret_cast<int*>(soff + kStreamMaxSegs);
+  const uint2* segs = a.segs + (int64_t)t * kStreamMaxSegs;
+  for (uint32_t i = threadIdx.x; i < nseg; i += kFinNT) {
+    const uint2 e = segs[i];
+    skey[i] = e.x;
+    sinfo[i] = e.y;
+  }
+  lds_barrier();
+  // segment keys (chunk << 3 | flush) are distinct: rank by counting
+  for (uint32_t i = threadIdx.x; i < nseg; i += kFinNT) {
+    const uint32_t ki = skey[i];
+    uint32_t rnk = 0;
+    for (uint32_t j = 0; j < nseg; ++j) rnk += skey[j] < ki ? 1u : 0u;
+    sorder[rnk] = (int)i;
+  }
+  lds_barrier();
+  uint32_t tot;
+  const uint32_t c = threadIdx.x < nseg ? (sinfo[sorder[threadIdx.x]] & 0xFFFFu) : 0u;
+  const uint32_t ex = block_exclusive_scan<kFinNT>(c, tmp, tot);
+  if (threadIdx.x < nseg) soff[threadIdx.x] = ex;
+  lds_barrier();
+  // stage the segments in token order: 32 threads per segment, 4 loads in flight each
+  const uint2* lists = a.lists + (int64_t)t * a.cap;
+  const int l32 = threadIdx.x & 31;
+  for (uint32_t sl = threadIdx.x >> 5; sl < nseg; sl += kFinNT / 32) {
+    const uint32_t inf = sinfo[sorder[sl]];
+    const uint32_t base = inf >> 16, cnt = inf & 0xFFFFu, o = soff[sl];
+    for (uint32_t e0 = 0; e0 < cnt; e0 += 4 * 32) {
+      uint2 v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const uint32_t e = e0 + u * 32 + l32;
+        v[u] = e < cnt ? lists[base + e] : make_uint2(0u, 0u);
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const uint32_t e = e0 + u * 32 + l32;
+        if (e < cnt) {
+          lkey[o + e] = v[u].x;
+          lidx[o + e] = (int)v[u].y;
+        }
+      }
+    }
+  }
+  lds_barrier();
+  const LdsSrc ls{lkey, lidx, (int)total};
+  refine_and_emit<kFinNT>(ls, 0u, 0, k, total, hist, tmp, &res, k,
+                          [&](uint32_t slot, uint32_t, int id) { out[slot] = id; });
+}
+
+// Rows the finalize could not select from their candidates: each is redone by
+// one workgroup, recomputing its scores batch by batch for every radix pass
+// and for the ordered compaction (nothing stored).  The grid is small and
+// fixed; workgroup g takes listed rows g, g + grid, ...
+template <int HT>
+__global__ void __launch_bounds__(kFinNT) stream_fallback_kernel(StreamArgs a) {
+  __shared__ uint32_t hist[kBins1];
+  __shared__ uint32_t tmp[kUnr * kFinNT / 64];
+  __shared__ BinSel res;
+  __shared__ __attribute__((aligned(16))) float sc[kFinBatch];
+
+  const uint32_t nredo = *a.redo_count;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int nl = lane & 15, grp = lane >> 4;
+  const uint32_t k = (uint32_t)a.k;
+  for (uint32_t r = blockIdx.x; r < nredo; r += gridDim.x) {
+    const int t = a.redo[r];
+    int b, pos;
+    row_seq_pos(a.g, t, b, pos);
+    const int n = pos + 1;
+    int32_t* out = a.idx + (int64_t)t * a.k;
+    RowScorer<HT> rs;
+    rs.init(a, t, nl, grp);
+    uint32_t P = 0u, need = k, cnt = (uint32_t)n;
+    int pbits = 0;
+    while (cnt != need && pbits < 32) {
+      const int bits = (pbits + 11 <= 22) ? 11 : 32 - pbits;
+      const int shift = 32 - pbits - bits;
+      const int nb = 1 << bits;
+      const uint32_t mask = (uint32_t)nb - 1u;
+      for (int i = threadIdx.x; i < nb; i += kFinNT) hist[i] = 0u;
+      for (int base = 0; base < n; base += kFinBatch) {
+        rs.stage(a, b, n, base, sc, wave, nl, grp);
+        lds_barrier();
+        const int nk = min(kFinBatch, n - base);
+        for (int i = threadIdx.x; i < nk; i += kFinNT) {
+          const uint32_t key = score_key(sc[i]);
+          if (pbits == 0 || (key >> (32 - pbits)) == P) atomicAdd(&hist[(key >> shift) & mask], 1u);
+        }
+        lds_barrier();
+      }
+      const BinSel s = select_bin<kFinNT>(hist, nb, need, tmp, &res);
+      P = (P << bits) | s.bin;
+      pbits += bits;
+      need -= s.above;
+      cnt = s.cnt;
+    }
+    uint32_t gt = 0u, eq = 0u;
+    for (int base = 0; base < n; base += kFinBatch) {
+      rs.stage(a, b, n, base, sc, wave, nl, grp);
+      lds_barrier();
+      uint32_t key[kUnr][4];
+      int id[kUnr][4];
+      bool ok[kUnr][4];
+#pragma unroll
+      for (int u = 0; u < kUnr; ++u)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int i = (u * kFinNT + (int)threadIdx.x) * 4 + j;
+          ok[u][j] = base + i < n;
+          key[u][j] = ok[u][j] ? score_key(sc[i]) : 0u;
+          id[u][j] = base + i;
+        }
+      // compact_batch's barriers also order these reads before the next stage's writes
+      auto to_out = [&](uint32_t slot, uint32_t, int id) { out[slot] = id; };
+      compact_batch<kFinNT>(key, id, ok, P, 32 - pbits, need, tmp, gt, eq, to_out);
+      if (gt + min(eq, need) >= k) break;
+    }
+    lds_barrier();                      // the next row's first stage overwrites sc
+  }
+}
+
+}  // namespace
+
+hipError_t launch_stream_gather(const StreamArgs& a, hipStream_t stream) {
+  const dim3 grid((unsigned)(((int64_t)a.umax * 8 + 255) / 256), (unsigned)a.g.num_seqs);
+  hipLaunchKernelGGL(stream_gather_kernel, grid, dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_stream_threshold(const StreamArgs& a, hipStream_t stream) {
+  hipLaunchKernelGGL(stream_threshold_kernel, dim3(a.g.num_rows), dim3(kThrNT), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_stream_finalize(const StreamArgs& a, hipStream_t stream) {
+  hipLaunchKernelGGL(stream_finalize_kernel, dim3(a.g.num_rows), dim3(kFinNT), 0, stream, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const dim3 grid(a.g.num_rows < kRedoGrid ? a.g.num_rows : kRedoGrid);
+  switch ((a.H_I + 15) / 16) {
+    case 1: hipLaunchKernelGGL(stream_fallback_kernel<1>, grid, dim3(kFinNT), 0, stream, a); break;
+    case 2: hipLaunchKernelGGL(stream_fallback_kernel<2>, grid, dim3(kFinNT), 0, stream, a); break;
+    case 3: hipLaunchKernelGGL(stream_fallback_kernel<3>, grid, dim3(kFinNT), 0, stream, a); break;
+    case 4: hipLaunchKernelGGL(stream_fallback_kernel<4>, grid, dim3(kFinNT), 0, stream, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace dsa

@@ -30,8 +30,8 @@ def _declared():
 
 def test_header_declares_the_four_calls():
     names = _declared()
-    for n in ("dsa_indexer", "dsa_topk", "dsa_sparse_attn", "dsa_decode", "dsa_prefill", "dsa_indexer_warmup",
-              "dsa_workspace_size",
+    for n in ("dsa_indexer", "dsa_topk", "dsa_sparse_attn", "dsa_decode", "dsa_prefill", "dsa_prefill_streaming",
+              "dsa_indexer_warmup", "dsa_workspace_size",
               "dsa_last_error"):
         assert n in names
 
@@ -156,6 +156,33 @@ def test_prefill_validation(lib):
     assert f(b, FAKE, need - 1) == _lib.DSA_ERR_WORKSPACE
     assert lib.dsa_workspace_size(_lib.DSA_WS_PREFILL, ctypes.byref(_batch()), 2048, 128, 512) == ctypes.c_size_t(-1).value
     assert lib.dsa_workspace_size(_lib.DSA_WS_DECODE, ctypes.byref(b), 2048, 128, 512) == ctypes.c_size_t(-1).value
+
+
+def test_prefill_streaming_validation(lib):
+    kidx, kv = _cache(128, seq=131072), _cache(1152, seq=131072)
+
+    def f(b, ws=None, n=0, k=2048, d_I=128, kidx=kidx):
+        return lib.dsa_prefill_streaming(ctypes.byref(b), FAKE, None, FAKE, ctypes.byref(kidx), None, 64, d_I, k,
+                                         FAKE, ctypes.byref(kv), None, 128, 576, 512, 0.04, FAKE, None, None, ws, n,
+                                         None)
+    assert f(_batch()) == _lib.DSA_ERR_SHAPE                   # q_start NULL: a decode batch
+    b = _batch(num_seqs=1, num_rows=4096, max_q=4096, max_len=131072, q_start=FAKE)
+    assert f(b, d_I=32, kidx=_cache(32, seq=131072)) == _lib.DSA_ERR_UNSUPPORTED
+    assert f(b, k=4096) == _lib.DSA_ERR_UNSUPPORTED
+    assert f(_batch(num_seqs=1, num_rows=8, max_q=8, max_len=262145, q_start=FAKE)) == _lib.DSA_ERR_UNSUPPORTED
+    need = lib.dsa_workspace_size(_lib.DSA_WS_PREFILL_STREAM, ctypes.byref(b), 2048, 128, 512)
+    dense = lib.dsa_workspace_size(_lib.DSA_WS_PREFILL, ctypes.byref(b), 2048, 128, 512)
+    # no [rows, max_len] score matrix: sampled scores (max_len / 16 per row) and
+    # candidate lists (32 * rank pairs per row, rank = 224 for k = 2048) instead
+    assert need < dense / 4
+    assert need >= 4096 * (131072 // 16) * 4 + 4096 * 32 * 224 * 8
+    assert f(b) == _lib.DSA_ERR_WORKSPACE
+    assert f(b, FAKE, need - 1) == _lib.DSA_ERR_WORKSPACE
+    assert f(b, FAKE + 16, need) == _lib.DSA_ERR_ALIGN
+    assert lib.dsa_workspace_size(_lib.DSA_WS_PREFILL_STREAM, ctypes.byref(b), 4096, 128, 512) == \
+        ctypes.c_size_t(-1).value
+    assert lib.dsa_workspace_size(_lib.DSA_WS_PREFILL_STREAM, ctypes.byref(_batch()), 2048, 128, 512) == \
+        ctypes.c_size_t(-1).value
 
 
 def test_short_context_workspace_has_no_scores(lib):

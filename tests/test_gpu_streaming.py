@@ -1,0 +1,204 @@
+"""GPU parity of the streaming prefill selection (dsa_prefill_streaming).
+
+The streaming path never stores the score matrix: a per-row threshold from the
+scores of every 16th token filters what leaves the indexer, and the exact
+top-k is selected among the survivors (rows left with too few or too many
+survivors are recomputed).  Its scores are the indexer's own, so its
+selection, and the attention over it, must equal dsa_prefill's bit for bit;
+on top of that it is checked against the oracle on sampled rows.  Crafted
+inputs force every branch: rows that keep every token (n <= capacity), rows
+thresholded on the sample, rows with fewer survivors than k, rows with more
+survivors than the capacity, and rows whose scores all tie.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+import sparse_attention_long_06_amd as dsa
+from tests.gpu_helpers import (DEV, announce, arrays_of, check_attention, check_topk_swaps, to_np)
+
+pytestmark = pytest.mark.gpu
+
+STRIDE = 16                                   # sampled tokens: every 16th
+
+
+def _rank(k):
+    return max((7 * k + 63) // 64, 64)
+
+
+def _cap(k):
+    return 2 * STRIDE * _rank(k)
+
+
+def _both(inp):
+    wl = inp.wl
+    batch = dsa.Batch.from_inputs(inp)
+    idx_p = torch.empty((inp.num_rows, wl.k), dtype=torch.int32, device=DEV)
+    idx_s = torch.empty_like(idx_p)
+    out_p, lse_p, _ = dsa.prefill(batch, inp.q8, inp.q_scale, inp.w, inp.k8, inp.k_scale, wl.k, inp.q, inp.kv,
+                                  inp.v, wl.scale, idx_out=idx_p, D_v=wl.D_v)
+    out_s, lse_s, _ = dsa.prefill_streaming(batch, inp.q8, inp.q_scale, inp.w, inp.k8, inp.k_scale, wl.k, inp.q,
+                                            inp.kv, inp.v, wl.scale, idx_out=idx_s, D_v=wl.D_v)
+    torch.cuda.synchronize()
+    return (idx_p, out_p, lse_p), (idx_s, out_s, lse_s)
+
+
+def _assert_same(p, s, what):
+    idx_p, out_p, lse_p = p
+    idx_s, out_s, lse_s = s
+    bad = (idx_p != idx_s).any(dim=1).nonzero().flatten().tolist()
+    assert not bad, f"{what}: rows {bad[:8]} select differently ({len(bad)} rows)"
+    assert torch.equal(out_p.view(torch.int16), out_s.view(torch.int16)), f"{what}: attention output differs"
+    assert torch.equal(lse_p, lse_s), f"{what}: lse differs"
+
+
+def _oracle_check(inp, idx, out, lse, rows, exact):
+    a = arrays_of(inp)
+    ref = oracle.run_rows(a, rows)
+    same = 0
+    for i, r in enumerate(rows):
+        if exact:
+            assert np.array_equal(idx[r], ref["idx"][i]), f"row {r}: selection not exact"
+            same += 1
+            check_attention(out[r], lse[r], ref["out"][i], ref["lse"][i], f"row {r}")
+        elif check_topk_swaps(idx[r], ref["idx"][i], ref["scores"][i], inp.wl.k):
+            same += 1
+            check_attention(out[r], lse[r], ref["out"][i], ref["lse"][i], f"row {r}")
+    assert same >= 0.9 * len(rows), f"only {same}/{len(rows)} rows selected the same set"
+    return ref
+
+
+CASES = [
+    # every row keeps every token (n <= capacity 7168)
+    W.SMALL_PREFILL,
+    # rows past the capacity take the sampled threshold; ragged last row tile and key chunk
+    W.PREFILL_32K.replace(name="prefill_L12003", seq_len=12003, seed=31, sample_rows=0),
+    # k = 512 (rank 64, capacity 2048), 8 indexer heads
+    W.PREFILL_32K.replace(name="prefill_L6000_k512_hi8", seq_len=6000, k=512, H_I=8, seed=32, sample_rows=0),
+    # two sequences behind a 64-token page table (sampled keys gathered through it)
+    W.PREFILL_32K.replace(name="prefill_b2_L9000_paged64", seqs=2, seq_len=9000, paged=True, block_size=64,
+                          seed=33, sample_rows=0),
+    # integer indexer: many exactly tied scores, selection bit-exact against the oracle
+    W.PREFILL_32K.replace(name="prefill_L9000_int", seq_len=9000, seed=34, sample_rows=0, integer_indexer=True),
+]
+
+
+@pytest.mark.parametrize("wl", CASES, ids=[w.name for w in CASES])
+def test_streaming_equals_prefill_and_oracle(wl):
+    announce("streaming prefill", wl.name)
+    inp = W.generate(wl, DEV)
+    p, s = _both(inp)
+    _assert_same(p, s, wl.name)
+    idx, out, lse = (to_np(x) for x in s)
+    n_rows = inp.num_rows
+    cap = _cap(wl.k)
+    always = [0, wl.k - 1, wl.k, min(cap, n_rows - 1), min(cap + 1, n_rows - 1), n_rows - 1]
+    rows = W.sample_rows(wl, n_rows, 24, always=tuple(r for r in always if r < n_rows))
+    _oracle_check(inp, idx, out, lse, rows, exact=wl.integer_indexer)
+
+
+def test_streaming_chunked_prefill_late_chunk():
+    """A chunk whose rows sit at positions 7500..9999 of a growing cache."""
+    wl = W.CHUNKED_128K.replace(name="chunked_prefill_L10000_c2500", seq_len=10000, chunk=2500, seed=35,
+                                sample_rows=0)
+    announce("streaming chunked prefill", wl.name, "chunk 3")
+    inp = W.generate(wl, DEV, chunk_index=3)
+    p, s = _both(inp)
+    _assert_same(p, s, wl.name)
+    idx, out, lse = (to_np(x) for x in s)
+    rows = W.sample_rows(wl, inp.num_rows, 16, always=(0, inp.num_rows - 1))
+    _oracle_check(inp, idx, out, lse, rows, exact=False)
+
+
+# ------------------------------------------------------------------ crafted rows for every fallback
+
+_INT = W.PREFILL_32K.replace(name="prefill_L9000_int_crafted", seq_len=9000, seed=36, sample_rows=0,
+                             integer_indexer=True)
+
+
+def _e4m3(v):
+    return torch.tensor(v, dtype=torch.float32).to(torch.float8_e4m3fn).view(torch.uint8).item()
+
+
+def _crafted(kind):
+    """Integer inputs with q8 = +1 and w = +1 everywhere (score = H_I * ReLU(sum_d k8[s, d])), then:
+    'underfill': sampled tokens (s % 16 == 0) score far above all others, so only
+                 rank < k tokens reach the sampled threshold;
+    'overflow':  sampled tokens score 0 and most others score > 0, so far more
+                 than the capacity reach it;
+    'zero_rows': every other query row is all zeros (every score 0: one big tie)."""
+    inp = W.generate(_INT, DEV)
+    one, three, mthree = _e4m3(1.0), _e4m3(3.0), _e4m3(-3.0)
+    if kind in ("underfill", "overflow"):
+        inp.q8.fill_(one)
+        inp.w.fill_(1.0)
+        k8 = inp.k8.view(-1, inp.k8.shape[-1])
+        sampled = torch.arange(k8.shape[0], device=DEV) % STRIDE == 0
+        if kind == "underfill":
+            # others: integers in [-1, 1] (row sums <= 128); sampled: all +3 (sum 384)
+            k8.copy_(torch.where(k8.view(torch.float8_e4m3fn).float().abs() > 1,
+                                 torch.full_like(k8, one), k8))
+            k8[sampled] = three
+        else:
+            # others: |values| so that most row sums are positive; sampled: all -3 (ReLU -> 0)
+            k8.copy_(k8.view(torch.float8_e4m3fn).float().abs().to(torch.float8_e4m3fn).view(torch.uint8))
+            k8[sampled] = mthree
+    elif kind == "zero_rows":
+        inp.q8[1::2] = 0
+    return inp
+
+
+@pytest.mark.parametrize("kind", ["underfill", "overflow", "zero_rows"])
+def test_streaming_fallbacks_bit_exact(kind):
+    announce("streaming prefill crafted", kind)
+    inp = _crafted(kind)
+    wl = inp.wl
+    p, s = _both(inp)
+    _assert_same(p, s, f"crafted {kind}")
+    idx, out, lse = (to_np(x) for x in s)
+    n_rows = inp.num_rows
+    cap = _cap(wl.k)
+    rows = [0, 1, wl.k - 1, wl.k, wl.k + 1, cap - 1, cap, cap + 1, cap + 2, n_rows - 2, n_rows - 1]
+    ref = _oracle_check(inp, idx, out, lse, rows, exact=True)
+    # the construction does what it claims on the rows past the capacity
+    for i, r in enumerate(rows):
+        n = r + 1
+        if n <= cap:
+            continue
+        sc = ref["scores"][i]
+        samp = np.arange(n) % STRIDE == 0
+        if kind == "underfill":
+            assert sc[~samp].max() < sc[samp].min() and _rank(wl.k) < wl.k
+        elif kind == "overflow":
+            assert (sc[samp] == 0).all() and (sc[~samp] > 0).all()
+            if n >= n_rows - 1:                       # 15/16 of 9000 tokens beat the sampled threshold
+                assert (sc[~samp] > 0).sum() > cap
+        elif r % 2 == 1:
+            assert (sc == 0).all()
+            assert np.array_equal(idx[r], np.arange(wl.k))
+
+
+def test_streaming_repeatable():
+    """Two calls give bit-identical results (the list order from atomics never shows)."""
+    wl = CASES[1]
+    announce("streaming prefill repeat", wl.name)
+    inp = W.generate(wl, DEV)
+    batch = dsa.Batch.from_inputs(inp)
+    res = []
+    for _ in range(2):
+        idx = torch.empty((inp.num_rows, wl.k), dtype=torch.int32, device=DEV)
+        out, lse, _ = dsa.prefill_streaming(batch, inp.q8, inp.q_scale, inp.w, inp.k8, inp.k_scale, wl.k, inp.q,
+                                            inp.kv, inp.v, wl.scale, idx_out=idx, D_v=wl.D_v)
+        torch.cuda.synchronize()
+        res.append((idx, out, lse))
+    _assert_same(res[0], res[1], "repeat")
+
+
+def test_streaming_short_context_is_dense():
+    wl = W.DENSE_PREFILL
+    announce("streaming prefill dense", wl.name)
+    inp = W.generate(wl, DEV)
+    p, s = _both(inp)
+    _assert_same(p, s, wl.name)
