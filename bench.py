@@ -345,8 +345,43 @@ def run_bench(args):
     return res, inp
 
 
+def _stream_stage_ms(step, reps):
+    """Per-stage times (indexer, selection, attention) of `reps` calls of a fused
+    entry point, from the four stage events the library records on its stream."""
+    from sparse_attention_long_06_amd import _lib
+    hip, lib = _hip(), _lib.load()
+    evs = []
+    for _ in range(4 * reps):
+        ev = ctypes.c_void_p()
+        assert hip.hipEventCreate(ctypes.byref(ev)) == 0
+        evs.append(ev.value)
+    for i in range(reps):
+        assert lib.dsa_set_stage_events((ctypes.c_void_p * 4)(*evs[4 * i: 4 * i + 4]), 4) == 0
+        step()
+    assert hip.hipDeviceSynchronize() == 0
+    f = ctypes.c_float()
+    per = {"indexer": [], "topk": [], "attention": []}
+    for i in range(reps):
+        e = evs[4 * i: 4 * i + 4]
+        for name, (a, b) in zip(per, [(0, 1), (1, 2), (2, 3)]):
+            assert hip.hipEventElapsedTime(ctypes.byref(f), ctypes.c_void_p(e[a]), ctypes.c_void_p(e[b])) == 0
+            per[name].append(f.value)
+    for ev in evs:
+        hip.hipEventDestroy(ctypes.c_void_p(ev))
+    return {k: sorted(v)[len(v) // 2] for k, v in per.items()}
+
+
+def _prefill_streaming_call(dsa, wl, inp, batch, out, lse, idx, ws):
+    return lambda: dsa.prefill_streaming(batch, inp.q8, inp.q_scale, inp.w, inp.k8, inp.k_scale, wl.k, inp.q,
+                                         inp.kv, inp.v, wl.scale, out=out, lse=lse, idx_out=idx, workspace=ws,
+                                         D_v=wl.D_v)
+
+
 def run_prefill(args):
-    """One step = indexer, top-k and sparse attention over every row of a causal prefill."""
+    """One step = indexer, top-k and sparse attention over every row of a causal
+    prefill: the three entry points in turn (--select staged, the score matrix
+    in HBM between them) or one dsa_prefill_streaming call (--select
+    streaming, no score matrix)."""
     import torch
 
     import workloads as W
@@ -361,32 +396,50 @@ def run_prefill(args):
     inp = W.generate(wl, dev)
     batch = dsa.Batch.from_inputs(inp)
     T = inp.num_rows
-    ld = (inp.max_len + 3) // 4 * 4
-    scores = torch.empty((T, ld), dtype=torch.float32, device=dev)
     idx = torch.empty((T, wl.k), dtype=torch.int32, device=dev)
     out = torch.empty((T, wl.H, wl.D_v), dtype=torch.bfloat16, device=dev)
     lse = torch.empty((T, wl.H), dtype=torch.float32, device=dev)
-    stages = {"indexer": lambda: dsa.indexer(batch, inp.q8, inp.q_scale, inp.w, inp.k8, inp.k_scale, scores=scores),
-              "topk": lambda: dsa.topk(batch, scores, wl.k, idx=idx),
-              "attention": lambda: dsa.sparse_attn(batch, inp.q, inp.kv, inp.v, wl.scale, idx, out=out, lse=lse,
-                                                   D_v=wl.D_v)}
-    for _ in range(args.warmup):
-        for fn in stages.values():
-            fn()
-    torch.cuda.synchronize()
-    print(f"[bench] timing {args.steps} prefill steps", file=sys.stderr, flush=True)
-    times = {k: [] for k in stages}
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        for name, fn in stages.items():
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record()
-            fn()
-            e1.record()
-            times[name].append((e0, e1))
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    st = {k: sum(a.elapsed_time(b) for a, b in v) / len(v) for k, v in times.items()}
+    if args.select == "streaming":
+        ws_n = dsa.workspace_size(dsa.DSA_WS_PREFILL_STREAM, batch, wl.k, wl.H, wl.D_v)
+        ws = torch.empty(ws_n, dtype=torch.uint8, device=dev)
+        step = _prefill_streaming_call(dsa, wl, inp, batch, out, lse, idx, ws)
+        for _ in range(args.warmup):
+            step()
+        torch.cuda.synchronize()
+        print(f"[bench] timing {args.steps} streaming prefill steps", file=sys.stderr, flush=True)
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            step()
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t0
+        st = _stream_stage_ms(step, max(3, min(args.steps, 10)))
+        mem = {"workspace_bytes": ws_n}
+    else:
+        ld = (inp.max_len + 3) // 4 * 4
+        scores = torch.empty((T, ld), dtype=torch.float32, device=dev)
+        stages = {"indexer": lambda: dsa.indexer(batch, inp.q8, inp.q_scale, inp.w, inp.k8, inp.k_scale,
+                                                 scores=scores),
+                  "topk": lambda: dsa.topk(batch, scores, wl.k, idx=idx),
+                  "attention": lambda: dsa.sparse_attn(batch, inp.q, inp.kv, inp.v, wl.scale, idx, out=out,
+                                                       lse=lse, D_v=wl.D_v)}
+        for _ in range(args.warmup):
+            for fn in stages.values():
+                fn()
+        torch.cuda.synchronize()
+        print(f"[bench] timing {args.steps} prefill steps", file=sys.stderr, flush=True)
+        times = {k: [] for k in stages}
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            for name, fn in stages.items():
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                fn()
+                e1.record()
+                times[name].append((e0, e1))
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t0
+        st = {k: sum(a.elapsed_time(b) for a, b in v) / len(v) for k, v in times.items()}
+        mem = {"score_matrix_bytes": T * ld * 4}
     _, pos = inp.row_positions()
     pairs = sum(p + 1 for p in pos)
     idx_flops = 2 * wl.H_I * wl.d_I * pairs
@@ -403,8 +456,9 @@ def run_prefill(args):
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp8-storage/bf16-mfma",
         "data": "synthetic (seeded N(0,1) draws, per-token e4m3fn quantised indexer q/k; bf16 latent KV)",
         "config": {"workload": wl.name, "rows": T, "context": wl.seq_len, "k": wl.k, "H_I": wl.H_I, "d_I": wl.d_I,
-                   "H": wl.H, "D": wl.D, "D_v": wl.D_v, "parallelism": "single GPU"},
+                   "H": wl.H, "D": wl.D, "D_v": wl.D_v, "selection": args.select, "parallelism": "single GPU"},
         "stages_ms": {k: round(v, 3) for k, v in st.items()},
+        "memory": mem,
         "indexer": {"causal_pairs": pairs, "TFLOP/s": round(idx_tf, 1), "fp8_peak_frac": round(idx_tf / 5000.0, 4),
                     "bf16_peak_frac": round(idx_tf / BF16_PEAK_TFLOPS, 4)},
         "attention": {"selected_rows": att_rows, "TFLOP/s": round(att_tf, 1),
@@ -431,15 +485,34 @@ def run_chunked(args, wl):
     cache = W.cache_of(first)
     st = {"indexer": 0.0, "topk": 0.0, "attention": 0.0}
     pairs = att_rows = rows = 0
+    peak_ws = 0
     for c in range(nchunks):
         inp = first if c == 0 else W.generate(wl, dev, chunk_index=c, cache=cache)
         batch = dsa.Batch.from_inputs(inp)
         T = inp.num_rows
-        ld = (inp.max_len + 3) // 4 * 4
-        scores = torch.empty((T, ld), dtype=torch.float32, device=dev)
         idx = torch.empty((T, wl.k), dtype=torch.int32, device=dev)
         out = torch.empty((T, wl.H, wl.D_v), dtype=torch.bfloat16, device=dev)
         lse = torch.empty((T, wl.H), dtype=torch.float32, device=dev)
+        if args.select == "streaming":
+            ws_n = dsa.workspace_size(dsa.DSA_WS_PREFILL_STREAM, batch, wl.k, wl.H, wl.D_v)
+            peak_ws = max(peak_ws, ws_n)
+            ws = torch.empty(ws_n, dtype=torch.uint8, device=dev)
+            step = _prefill_streaming_call(dsa, wl, inp, batch, out, lse, idx, ws)
+            step()                              # warm-up of this chunk's shapes
+            torch.cuda.synchronize()
+            for name, v in _stream_stage_ms(step, args.steps).items():
+                st[name] += v
+            _, pos = inp.row_positions()
+            pairs += sum(p + 1 for p in pos)
+            att_rows += sum(min(wl.k, p + 1) for p in pos)
+            rows += T
+            del ws, idx, out, lse
+            if c % 8 == 7:
+                print(f"[bench] chunk {c + 1}/{nchunks}", file=sys.stderr, flush=True)
+            continue
+        ld = (inp.max_len + 3) // 4 * 4
+        peak_ws = max(peak_ws, T * ld * 4)
+        scores = torch.empty((T, ld), dtype=torch.float32, device=dev)
         stages = {"indexer": lambda: dsa.indexer(batch, inp.q8, inp.q_scale, inp.w, inp.k8, inp.k_scale,
                                                  scores=scores),
                   "topk": lambda: dsa.topk(batch, scores, wl.k, idx=idx),
@@ -475,8 +548,9 @@ def run_chunked(args, wl):
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp8-storage/bf16-mfma",
         "data": "synthetic (seeded N(0,1) draws, per-token e4m3fn quantised indexer q/k; bf16 latent KV)",
         "config": {"workload": wl.name, "rows": rows, "context": wl.seq_len, "chunk": wl.chunk, "k": wl.k,
-                   "parallelism": "single GPU"},
+                   "selection": args.select, "parallelism": "single GPU"},
         "stages_ms": {k: round(v, 3) for k, v in st.items()},
+        "memory": {("workspace_bytes" if args.select == "streaming" else "score_matrix_bytes"): peak_ws},
         "indexer": {"causal_pairs": pairs, "TFLOP/s": round(idx_tf, 1), "bf16_peak_frac": round(idx_tf / BF16_PEAK_TFLOPS, 4)},
         "attention": {"selected_rows": att_rows, "TFLOP/s": round(att_tf, 1),
                       "bf16_peak_frac": round(att_tf / BF16_PEAK_TFLOPS, 4)},
@@ -663,6 +737,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="decode_b32_ctx128k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--select", choices=("staged", "streaming"), default="staged",
+                    help="prefill workloads: staged entry points with the score matrix, or dsa_prefill_streaming")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--copy-calibration", type=int, default=0)
     args = ap.parse_args()

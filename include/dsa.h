@@ -182,7 +182,7 @@ dsa_status dsa_prefill(const dsa_batch* batch, const uint8_t* q8, const float* q
  * matrix: the top-k selection streams out of the indexer (sider.ai "Sparse
  * attention that isn't sparse thinking", section "Matematik, Minimalist
  * Sürüm": selection that stays cache-aware).  Per row, a threshold on the
- * order (score desc, token asc) is taken from the scores of every 16th token;
+ * order (score desc, token asc) is taken from the scores of every 32nd token;
  * the indexer then keeps only the (score, token) pairs at or above it, and the
  * exact top-k is selected among those.  A row left with fewer than k such
  * pairs, or more than the candidate capacity, is recomputed exactly (slower,
@@ -190,8 +190,8 @@ dsa_status dsa_prefill(const dsa_batch* batch, const uint8_t* q8, const float* q
  * dsa_prefill's bit for bit.  Arguments and errors as dsa_prefill, plus
  * DSA_ERR_UNSUPPORTED unless d_I = 128, k <= 2048 and max_len <= 262144.
  * Workspace: dsa_workspace_size(DSA_WS_PREFILL_STREAM, ...) bytes, 256-byte
- * aligned: O(num_rows * (max_len / 16 + 32 * rank)) with rank = max(64,
- * ceil(7k/64)), instead of num_rows * max_len scores.  Stage events as
+ * aligned: O(num_rows * (max_len / 32 + 56 * rank)) with rank = max(64,
+ * ceil(k/16)), instead of num_rows * max_len scores.  Stage events as
  * dsa_prefill (the indexer stage covers the sampled and the filtered pass).
  */
 dsa_status dsa_prefill_streaming(const dsa_batch* batch, const uint8_t* q8, const float* q_scale,

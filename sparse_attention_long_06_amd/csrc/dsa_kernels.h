@@ -50,17 +50,18 @@ hipError_t launch_indexer(const IndexerArgs& a, int d_I, bool decode_layout, boo
 // The threshold of a row comes from the scores of every kStreamStride-th
 // token; the filtered indexer keeps the pairs at or above it in LDS buffers of
 // kStreamLds entries per (wave, row) and flushes them as segments.
-constexpr int kStreamShift = 4;
+constexpr int kStreamShift = 5;
 constexpr int kStreamStride = 1 << kStreamShift;
 constexpr int kStreamLds = 448;
 constexpr int kStreamMaxSegs = 512;
 constexpr int kStreamMaxK = 2048;
 constexpr int kStreamMaxLen = 262144;
 
-// Rank of the threshold among a row's sampled scores, and the candidate
-// capacity per row (twice the expected count kStreamStride * rank).
-__host__ __device__ constexpr int stream_rank(int k) { return (7 * k + 63) / 64 > 64 ? (7 * k + 63) / 64 : 64; }
-__host__ __device__ constexpr int stream_cap(int k) { return 2 * kStreamStride * stream_rank(k); }
+// Rank of the threshold among a row's sampled scores (about k/16, at least
+// 64), and the candidate capacity per row (1.75 times the expected count
+// kStreamStride * rank; 7168 for k = 2048).
+__host__ __device__ constexpr int stream_rank(int k) { return (k + 15) / 16 > 64 ? (k + 15) / 16 : 64; }
+__host__ __device__ constexpr int stream_cap(int k) { return 56 * stream_rank(k); }
 
 hipError_t launch_indexer_stream(const IndexerArgs& a, hipStream_t stream);
 

@@ -557,26 +557,38 @@ __global__ void __launch_bounds__(256) indexer_prefill_ring_kernel(IndexerArgs a
     }
   }
   uint2* const mycand = &cand[FILT ? wave * R * kStreamLds : 0];
-  // Move row r's buffered pairs to its list: one 64-bit atomic reserves the
-  // space and the segment number, then the pairs and the segment record
-  // (chunk, flush number, base, count) are stored.  Pairs past the row's
-  // capacity are dropped; the finalize sees the total and recomputes the row.
-  auto flush = [&](int r) {
-    const uint32_t c = ccnt[r];
-    if (c == 0u) return;
-    const int64_t t = trow[r];
+  // Move the buffered pairs of the rows in `which` (bit r) to their lists.
+  // Lane r reserves row r's space and segment number with a 64-bit atomic (one
+  // instruction, one round trip for both rows), then the pairs and each
+  // segment record (chunk, flush number, base, count) are stored.  Pairs past
+  // the row's capacity are dropped; the finalize sees the total and
+  // recomputes the row.
+  static_assert(R == 2, "flush reserves two rows with one atomic");
+  auto flush = [&](uint32_t which) {
+    const uint32_t act = (which & 1u & (ccnt[0] ? 1u : 0u)) | (which & 2u & (ccnt[1] ? 2u : 0u));
+    if (!act) return;
     unsigned long long old = 0ull;
-    if (lane == 0) old = atomicAdd(&a.rowinfo[t], (1ull << 32) | (unsigned long long)c);
-    const uint32_t base = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)old);
-    const uint32_t seg = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(old >> 32));
-    const uint2* src = mycand + r * kStreamLds;
-    uint2* dst = a.lists + t * a.cap;
-    for (uint32_t i = lane; i < c; i += 64)
-      if (base + i < (uint32_t)a.cap) dst[base + i] = src[i];
-    if (lane == 0 && seg < (uint32_t)kStreamMaxSegs)
-      a.segs[t * kStreamMaxSegs + seg] = make_uint2(((uint32_t)chunk_id << 3) | cfl[r], (base << 16) | c);
-    ccnt[r] = 0u;
-    cfl[r] += 1u;
+    if (lane < R && ((act >> lane) & 1u)) {
+      const int64_t t = lane == 0 ? trow[0] : trow[1];
+      const uint32_t c = lane == 0 ? ccnt[0] : ccnt[1];
+      old = atomicAdd(&a.rowinfo[t], (1ull << 32) | (unsigned long long)c);
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      if (!((act >> r) & 1u)) continue;
+      const uint32_t base = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)old, r);
+      const uint32_t seg = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(old >> 32), r);
+      const uint32_t c = ccnt[r];
+      const int64_t t = trow[r];
+      const uint2* src = mycand + r * kStreamLds;
+      uint2* dst = a.lists + t * a.cap;
+      for (uint32_t i = lane; i < c; i += 64)
+        if (base + i < (uint32_t)a.cap) dst[base + i] = src[i];
+      if (lane == 0 && seg < (uint32_t)kStreamMaxSegs)
+        a.segs[t * kStreamMaxSegs + seg] = make_uint2(((uint32_t)chunk_id << 3) | cfl[r], (base << 16) | c);
+      ccnt[r] = 0u;
+      cfl[r] += 1u;
+    }
   };
   __builtin_amdgcn_s_waitcnt(0x0F70);                 // rows and ring prologue are in
 
@@ -599,8 +611,16 @@ __global__ void __launch_bounds__(256) indexer_prefill_ring_kernel(IndexerArgs a
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
     if (more) issue(m + kPreRing - 1);
+    if constexpr (FILT) {
+      // room for this slot's pairs (at most kPreKeys per row), so the
+      // per-slot append below needs no capacity check
+      const uint32_t full = (ccnt[0] > (uint32_t)(kStreamLds - kPreKeys) ? 1u : 0u) |
+                            (ccnt[1] > (uint32_t)(kStreamLds - kPreKeys) ? 2u : 0u);
+      if (full) flush(full);
+    }
 
     const char* slot = &ring[m % kPreRing][0];
+    float fv[FILT ? kPreKeys / 16 : 1][R];              // FILT: scores of key group j, row r
 #pragma unroll
     for (int j = 0; j < kPreKeys / 16; ++j) {
       Frag<DI> kf;
@@ -619,32 +639,32 @@ __global__ void __launch_bounds__(256) indexer_prefill_ring_kernel(IndexerArgs a
           for (int i = 0; i < 4; ++i) part = fmaf(wq[r][ht][i], relu(acc[i]), part);
         }
         part = group_sum(part);
-        if constexpr (FILT) {
-          // keep (key, token) when s <= p and (key, ~s) reaches the threshold;
-          // lanes 0-15 hold keys 16j .. 16j+15 of the slot in order, so the
-          // buffer (and each segment) stays in token order
-          const uint32_t key = score_key(part * ks);
-          const unsigned long long comp = ((unsigned long long)key << 32) | (uint32_t)~(uint32_t)s;
-          const bool keep = grp == 0 && s <= rpos[r] && comp >= rthr[r];
-          const unsigned long long m64 = __ballot(keep);
-          if (m64) {                                  // uniform
-            const uint32_t c = (uint32_t)__popcll(m64);
-            if (ccnt[r] + c > (uint32_t)kStreamLds) flush(r);
-            const uint32_t before = __builtin_amdgcn_mbcnt_hi((uint32_t)(m64 >> 32),
-                                                              __builtin_amdgcn_mbcnt_lo((uint32_t)m64, 0u));
-            if (keep) mycand[r * kStreamLds + ccnt[r] + before] = make_uint2(key, (uint32_t)s);
-            ccnt[r] += c;
-          }
-        } else {
-          if (grp == 0 && s < kend && trow[r] >= 0) a.scores[trow[r] * a.ld + s] = part * ks;
-        }
+        if constexpr (FILT)
+          fv[j][r] = part * ks;                       // every lane holds the score of key 16j + nl
+        else if (grp == 0 && s < kend && trow[r] >= 0)
+          a.scores[trow[r] * a.ld + s] = part * ks;
+      }
+    }
+    if constexpr (FILT) {
+      // lane (g, l) takes key 16g + l of the slot, so the 64 lanes hold the
+      // slot's keys in token order: one ballot and one append per row keep
+      // (key, token) when token <= p and (key, ~token) reaches the threshold
+      const int s = kbeg + m * kPreKeys + lane;
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const float x = grp == 0 ? fv[0][r] : grp == 1 ? fv[1][r] : grp == 2 ? fv[2][r] : fv[3][r];
+        const uint32_t key = score_key(x);
+        const unsigned long long comp = ((unsigned long long)key << 32) | (uint32_t)~(uint32_t)s;
+        const bool keep = s <= rpos[r] && comp >= rthr[r];
+        const unsigned long long m64 = __ballot(keep);
+        const uint32_t before = __builtin_amdgcn_mbcnt_hi((uint32_t)(m64 >> 32),
+                                                          __builtin_amdgcn_mbcnt_lo((uint32_t)m64, 0u));
+        if (keep) mycand[r * kStreamLds + ccnt[r] + before] = make_uint2(key, (uint32_t)s);
+        ccnt[r] += (uint32_t)__popcll(m64);
       }
     }
   }
-  if constexpr (FILT) {
-#pragma unroll
-    for (int r = 0; r < R; ++r) flush(r);
-  }
+  if constexpr (FILT) flush(3u);
 }
 
 template <int HT, int DI>

@@ -14,7 +14,8 @@
 //   gather     every kStreamStride-th token's index key (and scale) of each
 //              sequence, compacted, so the prefill indexer can score them;
 //   [indexer over the compacted keys: the sampled scores]
-//   threshold  per row, thr = the rank-th largest c over its sampled tokens;
+//   threshold  per row, thr = the rank-th largest c over its sampled tokens
+//              (or the lower edge of its 22-bit key bin when few samples share it);
 //              rows with n <= cap take thr = 0 (every token), rows with
 //              n <= k need none;
 //   [filtered indexer: pairs with c >= thr go to segment lists]
@@ -50,12 +51,30 @@ __global__ void __launch_bounds__(256) stream_gather_kernel(StreamArgs a) {
 }
 
 constexpr int kThrNT = 256;
+constexpr int kThrMaxSamples = kStreamMaxLen / kStreamStride;
+
+// Order keys in LDS; element i is sampled token i.
+struct LdsKeySrc {
+  const uint32_t* key;
+  int n;
+  __device__ int size() const { return n; }
+  __device__ __forceinline__ void load4(int i, uint32_t (&k)[4], int (&d)[4], bool (&ok)[4]) const {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      ok[j] = i + j < n;
+      k[j] = ok[j] ? key[i + j] : 0u;
+      d[j] = i + j;
+    }
+  }
+  __device__ __forceinline__ void load4_full(int i, uint32_t (&k)[4], int (&d)[4], bool (&ok)[4]) const { load4(i, k, d, ok); }
+};
 
 __global__ void __launch_bounds__(kThrNT) stream_threshold_kernel(StreamArgs a) {
   __shared__ uint32_t hist[kBins1];
   __shared__ uint32_t tmp[kUnr * kThrNT / 64];
   __shared__ BinSel res;
   __shared__ unsigned long long tmin;
+  __shared__ __attribute__((aligned(16))) uint32_t skeys[kThrMaxSamples];
 
   const int t = blockIdx.x;
   int b, pos;
@@ -70,32 +89,68 @@ __global__ void __launch_bounds__(kThrNT) stream_threshold_kernel(StreamArgs a) 
     thr = 0ull;                                          // every token is a candidate
   } else {
     // the rank-th largest pair order among the sampled tokens u <= p >> shift
-    // (token u << shift); m > 2 * rank because n > cap
+    // (token u << shift); m > 1.75 * rank because n > cap.  The row's sampled
+    // scores are read once (all loads in flight) into LDS as order keys.
     const int m = (pos >> kStreamShift) + 1;
-    const RowSrc src{a.samp + (int64_t)t * a.ld_samp, m, 0};
+    const float4* row = reinterpret_cast<const float4*>(a.samp + (int64_t)t * a.ld_samp);
+    const int n4 = (m + 3) >> 2;
+    constexpr int PER = kThrMaxSamples / (4 * kThrNT);
+    float4 v[PER];
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int i = u * kThrNT + (int)threadIdx.x;
+      if (i < n4) v[u] = row[i];
+    }
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int i = u * kThrNT + (int)threadIdx.x;
+      if (i < n4)
+        reinterpret_cast<uint4*>(skeys)[i] = make_uint4(score_key(v[u].x), score_key(v[u].y), score_key(v[u].z),
+                                                        score_key(v[u].w));
+    }
     if (threadIdx.x == 0) tmin = ~0ull;
     lds_barrier();
-    const uint32_t r = (uint32_t)a.rank;
-    refine_and_emit<kThrNT>(src, 0u, 0, r, (uint32_t)m, hist, tmp, &res, r,
-                            [&](uint32_t, uint32_t key, int id) {
-                              const uint32_t tok = (uint32_t)id << kStreamShift;
-                              atomicMin(&tmin, ((unsigned long long)key << 32) | (uint32_t)~tok);
-                            });
-    lds_barrier();
-    thr = tmin;
+    const LdsKeySrc src{skeys, m};
+    // Two radix passes (22 key bits).  When the boundary bin then holds only a
+    // few samples, its lower edge is the threshold (every token whose key
+    // reaches it is kept: a few more candidates than the exact rank-th pair,
+    // never fewer); otherwise (many equal keys) the exact rank-th pair order,
+    // token index included, bounds the candidates.
+    uint32_t P = 0u, need = (uint32_t)a.rank, cnt = (uint32_t)m;
+    int pbits = 0;
+    for (int pass = 0; pass < 2 && cnt != need; ++pass) {
+      hist_pass<kThrNT>(src, hist, P, pbits, 32 - pbits - kBins1Bits, kBins1Bits);
+      const BinSel sb = select_bin<kThrNT>(hist, kBins1, need, tmp, &res);
+      P = (P << kBins1Bits) | sb.bin;
+      pbits += kBins1Bits;
+      need -= sb.above;
+      cnt = sb.cnt;
+    }
+    if (cnt == need || cnt <= 8u) {
+      thr = (unsigned long long)(P << (32 - pbits)) << 32;
+    } else {
+      refine_and_emit<kThrNT>(src, P, pbits, need, cnt, hist, tmp, &res, (uint32_t)a.rank,
+                              [&](uint32_t, uint32_t key, int id) {
+                                const uint32_t tok = (uint32_t)id << kStreamShift;
+                                atomicMin(&tmin, ((unsigned long long)key << 32) | (uint32_t)~tok);
+                              });
+      lds_barrier();
+      thr = tmin;
+    }
   }
   if (threadIdx.x == 0) a.thr[t] = thr;
 }
 
-constexpr int kFinNT = 512;
-constexpr int kFinBatch = kFinNT * 4 * kUnr;             // tokens per recomputed batch (fallback)
+constexpr int kFinNT = 256;                              // finalize
+constexpr int kRedoNT = 512;                             // fallback
+constexpr int kRedoBatch = kRedoNT * 4 * kUnr;           // tokens per recomputed batch (fallback)
 // LDS layout of the batch buffer on the candidate path: keys [cap], tokens
 // [cap], then the segment tables
 constexpr int kFinSegOff = 8 * 7168;
 static_assert(stream_cap(kStreamMaxK) <= 7168, "candidate pairs must fit before the segment tables");
 constexpr int kRedoGrid = 256;
 
-// Scores of tokens [base, base + kFinBatch) of row t (those < n) into sc,
+// Scores of tokens [base, base + kRedoBatch) of row t (those < n) into sc,
 // with the arithmetic of the prefill indexer in the same order, so that they
 // equal the scores the indexer produces bit for bit.
 template <int HT>
@@ -125,9 +180,9 @@ struct RowScorer {
   }
 
   __device__ void stage(const StreamArgs& a, int b, int n, int base, float* sc, int wave, int nl, int grp) const {
-    const int nk = min(kFinBatch, n - base);
+    const int nk = min(kRedoBatch, n - base);
     const int ngroups = (nk + 15) / 16;
-    for (int gi = wave; gi < ngroups; gi += kFinNT / 64) {
+    for (int gi = wave; gi < ngroups; gi += kRedoNT / 64) {
       const int s = base + gi * 16 + nl;
       const int sl = min(s, n - 1);
       Frag<128> kf;
@@ -147,12 +202,12 @@ struct RowScorer {
   }
 };
 
-__global__ void __launch_bounds__(kFinNT) __attribute__((amdgpu_waves_per_eu(4)))
-stream_finalize_kernel(StreamArgs a) {
+__global__ void __launch_bounds__(kFinNT) stream_finalize_kernel(StreamArgs a) {
   __shared__ uint32_t hist[kBins1];
   __shared__ uint32_t tmp[kUnr * kFinNT / 64];
   __shared__ BinSel res;
   __shared__ __attribute__((aligned(16))) char big[kFinSegOff + 16 * kStreamMaxSegs];
+  static_assert(kStreamMaxSegs == 2 * kFinNT, "two segments per thread in the offset scan");
 
   const int t = blockIdx.x;
   int b, pos;
@@ -190,13 +245,19 @@ stream_finalize_kernel(StreamArgs a) {
     for (uint32_t j = 0; j < nseg; ++j) rnk += skey[j] < ki ? 1u : 0u;
     sorder[rnk] = (int)i;
   }
+  for (int i = threadIdx.x; i < kBins1; i += kFinNT) hist[i] = 0u;
   lds_barrier();
+  // offsets in sorted order, two segments per thread
   uint32_t tot;
-  const uint32_t c = threadIdx.x < nseg ? (sinfo[sorder[threadIdx.x]] & 0xFFFFu) : 0u;
-  const uint32_t ex = block_exclusive_scan<kFinNT>(c, tmp, tot);
-  if (threadIdx.x < nseg) soff[threadIdx.x] = ex;
+  const uint32_t j0 = 2 * threadIdx.x;
+  const uint32_t c0 = j0 < nseg ? (sinfo[sorder[j0]] & 0xFFFFu) : 0u;
+  const uint32_t c1 = j0 + 1 < nseg ? (sinfo[sorder[j0 + 1]] & 0xFFFFu) : 0u;
+  const uint32_t ex = block_exclusive_scan<kFinNT>(c0 + c1, tmp, tot);
+  if (j0 < nseg) soff[j0] = ex;
+  if (j0 + 1 < nseg) soff[j0 + 1] = ex + c0;
   lds_barrier();
-  // stage the segments in token order: 32 threads per segment, 4 loads in flight each
+  // stage the segments in token order: 32 threads per segment, 4 loads in
+  // flight each; every pair also counts its top key bits (the first radix pass)
   const uint2* lists = a.lists + (int64_t)t * a.cap;
   const int l32 = threadIdx.x & 31;
   for (uint32_t sl = threadIdx.x >> 5; sl < nseg; sl += kFinNT / 32) {
@@ -215,13 +276,15 @@ stream_finalize_kernel(StreamArgs a) {
         if (e < cnt) {
           lkey[o + e] = v[u].x;
           lidx[o + e] = (int)v[u].y;
+          atomicAdd(&hist[v[u].x >> (32 - kBins1Bits)], 1u);
         }
       }
     }
   }
   lds_barrier();
+  const BinSel s1 = select_bin<kFinNT>(hist, kBins1, k, tmp, &res);
   const LdsSrc ls{lkey, lidx, (int)total};
-  refine_and_emit<kFinNT>(ls, 0u, 0, k, total, hist, tmp, &res, k,
+  refine_and_emit<kFinNT>(ls, s1.bin, kBins1Bits, k - s1.above, s1.cnt, hist, tmp, &res, k,
                           [&](uint32_t slot, uint32_t, int id) { out[slot] = id; });
 }
 
@@ -230,11 +293,11 @@ stream_finalize_kernel(StreamArgs a) {
 // and for the ordered compaction (nothing stored).  The grid is small and
 // fixed; workgroup g takes listed rows g, g + grid, ...
 template <int HT>
-__global__ void __launch_bounds__(kFinNT) stream_fallback_kernel(StreamArgs a) {
+__global__ void __launch_bounds__(kRedoNT) stream_fallback_kernel(StreamArgs a) {
   __shared__ uint32_t hist[kBins1];
-  __shared__ uint32_t tmp[kUnr * kFinNT / 64];
+  __shared__ uint32_t tmp[kUnr * kRedoNT / 64];
   __shared__ BinSel res;
-  __shared__ __attribute__((aligned(16))) float sc[kFinBatch];
+  __shared__ __attribute__((aligned(16))) float sc[kRedoBatch];
 
   const uint32_t nredo = *a.redo_count;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -255,25 +318,25 @@ __global__ void __launch_bounds__(kFinNT) stream_fallback_kernel(StreamArgs a) {
       const int shift = 32 - pbits - bits;
       const int nb = 1 << bits;
       const uint32_t mask = (uint32_t)nb - 1u;
-      for (int i = threadIdx.x; i < nb; i += kFinNT) hist[i] = 0u;
-      for (int base = 0; base < n; base += kFinBatch) {
+      for (int i = threadIdx.x; i < nb; i += kRedoNT) hist[i] = 0u;
+      for (int base = 0; base < n; base += kRedoBatch) {
         rs.stage(a, b, n, base, sc, wave, nl, grp);
         lds_barrier();
-        const int nk = min(kFinBatch, n - base);
-        for (int i = threadIdx.x; i < nk; i += kFinNT) {
+        const int nk = min(kRedoBatch, n - base);
+        for (int i = threadIdx.x; i < nk; i += kRedoNT) {
           const uint32_t key = score_key(sc[i]);
           if (pbits == 0 || (key >> (32 - pbits)) == P) atomicAdd(&hist[(key >> shift) & mask], 1u);
         }
         lds_barrier();
       }
-      const BinSel s = select_bin<kFinNT>(hist, nb, need, tmp, &res);
+      const BinSel s = select_bin<kRedoNT>(hist, nb, need, tmp, &res);
       P = (P << bits) | s.bin;
       pbits += bits;
       need -= s.above;
       cnt = s.cnt;
     }
     uint32_t gt = 0u, eq = 0u;
-    for (int base = 0; base < n; base += kFinBatch) {
+    for (int base = 0; base < n; base += kRedoBatch) {
       rs.stage(a, b, n, base, sc, wave, nl, grp);
       lds_barrier();
       uint32_t key[kUnr][4];
@@ -283,14 +346,14 @@ __global__ void __launch_bounds__(kFinNT) stream_fallback_kernel(StreamArgs a) {
       for (int u = 0; u < kUnr; ++u)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const int i = (u * kFinNT + (int)threadIdx.x) * 4 + j;
+          const int i = (u * kRedoNT + (int)threadIdx.x) * 4 + j;
           ok[u][j] = base + i < n;
           key[u][j] = ok[u][j] ? score_key(sc[i]) : 0u;
           id[u][j] = base + i;
         }
       // compact_batch's barriers also order these reads before the next stage's writes
       auto to_out = [&](uint32_t slot, uint32_t, int id) { out[slot] = id; };
-      compact_batch<kFinNT>(key, id, ok, P, 32 - pbits, need, tmp, gt, eq, to_out);
+      compact_batch<kRedoNT>(key, id, ok, P, 32 - pbits, need, tmp, gt, eq, to_out);
       if (gt + min(eq, need) >= k) break;
     }
     lds_barrier();                      // the next row's first stage overwrites sc
@@ -316,10 +379,10 @@ hipError_t launch_stream_finalize(const StreamArgs& a, hipStream_t stream) {
   if (e != hipSuccess) return e;
   const dim3 grid(a.g.num_rows < kRedoGrid ? a.g.num_rows : kRedoGrid);
   switch ((a.H_I + 15) / 16) {
-    case 1: hipLaunchKernelGGL(stream_fallback_kernel<1>, grid, dim3(kFinNT), 0, stream, a); break;
-    case 2: hipLaunchKernelGGL(stream_fallback_kernel<2>, grid, dim3(kFinNT), 0, stream, a); break;
-    case 3: hipLaunchKernelGGL(stream_fallback_kernel<3>, grid, dim3(kFinNT), 0, stream, a); break;
-    case 4: hipLaunchKernelGGL(stream_fallback_kernel<4>, grid, dim3(kFinNT), 0, stream, a); break;
+    case 1: hipLaunchKernelGGL(stream_fallback_kernel<1>, grid, dim3(kRedoNT), 0, stream, a); break;
+    case 2: hipLaunchKernelGGL(stream_fallback_kernel<2>, grid, dim3(kRedoNT), 0, stream, a); break;
+    case 3: hipLaunchKernelGGL(stream_fallback_kernel<3>, grid, dim3(kRedoNT), 0, stream, a); break;
+    case 4: hipLaunchKernelGGL(stream_fallback_kernel<4>, grid, dim3(kRedoNT), 0, stream, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

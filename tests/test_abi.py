@@ -172,10 +172,10 @@ def test_prefill_streaming_validation(lib):
     assert f(_batch(num_seqs=1, num_rows=8, max_q=8, max_len=262145, q_start=FAKE)) == _lib.DSA_ERR_UNSUPPORTED
     need = lib.dsa_workspace_size(_lib.DSA_WS_PREFILL_STREAM, ctypes.byref(b), 2048, 128, 512)
     dense = lib.dsa_workspace_size(_lib.DSA_WS_PREFILL, ctypes.byref(b), 2048, 128, 512)
-    # no [rows, max_len] score matrix: sampled scores (max_len / 16 per row) and
-    # candidate lists (32 * rank pairs per row, rank = 224 for k = 2048) instead
+    # no [rows, max_len] score matrix: sampled scores (max_len / 32 per row) and
+    # candidate lists (56 * rank pairs per row, rank = 128 for k = 2048) instead
     assert need < dense / 4
-    assert need >= 4096 * (131072 // 16) * 4 + 4096 * 32 * 224 * 8
+    assert need >= 4096 * (131072 // 32) * 4 + 4096 * 56 * 128 * 8
     assert f(b) == _lib.DSA_ERR_WORKSPACE
     assert f(b, FAKE, need - 1) == _lib.DSA_ERR_WORKSPACE
     assert f(b, FAKE + 16, need) == _lib.DSA_ERR_ALIGN
