@@ -737,7 +737,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="decode_b32_ctx128k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--select", choices=("staged", "streaming"), default="staged",
+    ap.add_argument("--select", choices=("staged", "streaming"), default="streaming",
                     help="prefill workloads: staged entry points with the score matrix, or dsa_prefill_streaming")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--copy-calibration", type=int, default=0)
