@@ -35,10 +35,11 @@ BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, vendor figure
 # kernel sources they were taken on; any change to them reports null.
 INDEXER_COUNTERS = {
     "workload": "decode_b32_ctx128k",
-    "sources": ["sparse_attention_long_06_amd/csrc/indexer.hip", "sparse_attention_long_06_amd/csrc/dsa_common.h",
-                "sparse_attention_long_06_amd/csrc/dsa_kernels.h", "sparse_attention_long_06_amd/csrc/api.hip"],
-    "sha256": "bd09ef1138121d5f279aebb40c71fed797b6eceda9736cf3b6c1c186393804e1",
-    "fetch_kib": 272608.1,
+    "sources": ["sparse_attention_long_06_amd/csrc/indexer.hip", "sparse_attention_long_06_amd/csrc/idx_math.h",
+                "sparse_attention_long_06_amd/csrc/dsa_common.h", "sparse_attention_long_06_amd/csrc/dsa_kernels.h",
+                "sparse_attention_long_06_amd/csrc/api.hip"],
+    "sha256": "36bb081f79ca98a016b85b7e1a0d8e0527c9fab9e07f02d6de0e2807c9de46ec",
+    "fetch_kib": 272619.9,
     "write_kib": 17231.0,
     "fetch_scale": 2.0,
     "write_scale": 1.0,
