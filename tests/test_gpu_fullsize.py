@@ -8,6 +8,9 @@ The oracle recomputes sampled rows one by one on the host:
     around the k = 2048 boundary and the last row;
   * 128K chunked prefill: every chunk runs; sampled rows of a spread of chunks
     (first and last row of each sampled chunk included) are checked.
+The prefill workloads also run dsa_prefill_streaming (the configuration the
+benchmark times for them), whose selection, output and lse must equal the
+staged calls' bit for bit on every row of every chunk.
 Rules as in test_gpu_parity.py.
 """
 import time
@@ -37,6 +40,20 @@ def _check_rows(ref, rows, idx, out, lse, k, min_same=0.9, what=""):
             check_attention(out[r], lse[r], ref["out"][i], ref["lse"][i], f"{what} row {r}")
     assert same >= min_same * len(rows), f"{what}: only {same}/{len(rows)} rows selected the same set"
     return same
+
+
+def _streaming_equals(inp, batch, idx, out, lse, what):
+    """dsa_prefill_streaming against the staged results, every row, bit for bit."""
+    wl = inp.wl
+    idx_s = torch.empty_like(idx)
+    out_s, lse_s, _ = dsa.prefill_streaming(batch, inp.q8, inp.q_scale, inp.w, inp.k8, inp.k_scale, wl.k, inp.q,
+                                            inp.kv, inp.v, wl.scale, idx_out=idx_s, D_v=wl.D_v)
+    torch.cuda.synchronize()
+    bad = (idx_s != idx).any(dim=1).nonzero().flatten().tolist()
+    assert not bad, f"{what}: streaming selection differs on rows {bad[:8]} ({len(bad)} rows)"
+    assert torch.equal(out_s.view(torch.int16), out.view(torch.int16)), f"{what}: streaming output differs"
+    assert torch.equal(lse_s, lse), f"{what}: streaming lse differs"
+    del idx_s, out_s, lse_s
 
 
 @pytest.mark.parametrize("wl", [W.DECODE_128K, W.PAGED_DECODE_MIXED], ids=lambda w: w.name)
@@ -71,7 +88,7 @@ def test_prefill_32k_sampled_rows():
     scores = dsa.indexer(batch, inp.q8, inp.q_scale, inp.w, inp.k8, inp.k_scale)
     idx = dsa.topk(batch, scores, wl.k)
     out, lse = dsa.sparse_attn(batch, inp.q, inp.kv, inp.v, wl.scale, idx, D_v=wl.D_v)
-    torch.cuda.synchronize()
+    _streaming_equals(inp, batch, idx, out, lse, wl.name)
     _log(wl.name, "gpu done", f"{time.time() - t0:.1f}s")
     rows = W.sample_rows(wl, inp.num_rows, wl.sample_rows, always=(0, 1, 2046, 2047, 2048, 2049, 32767))
     rows_t = torch.tensor(rows, device=DEV)
@@ -106,7 +123,7 @@ def test_chunked_prefill_128k_sampled_chunks():
         scores = dsa.indexer(batch, inp.q8, inp.q_scale, inp.w, inp.k8, inp.k_scale)
         idx = dsa.topk(batch, scores, wl.k)
         out, lse = dsa.sparse_attn(batch, inp.q, inp.kv, inp.v, wl.scale, idx, D_v=wl.D_v)
-        torch.cuda.synchronize()
+        _streaming_equals(inp, batch, idx, out, lse, f"chunk {c}")
         if c not in check_chunks:
             continue
         rows = W.sample_rows(wl, inp.num_rows, wl.sample_rows, always=(0, inp.num_rows - 1))

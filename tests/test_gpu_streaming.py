@@ -82,6 +82,10 @@ CASES = [
                           seed=33, sample_rows=0),
     # integer indexer: many exactly tied scores, selection bit-exact against the oracle
     W.PREFILL_32K.replace(name="prefill_L9000_int", seq_len=9000, seed=34, sample_rows=0, integer_indexer=True),
+    # the other head-tile counts of the filtered kernel: 16 heads with k = 64 (rank 64, capacity 3584), 48 heads
+    # with k = 1024 (rank 64, capacity 3584)
+    W.PREFILL_32K.replace(name="prefill_L5000_k64_hi16", seq_len=5000, k=64, H_I=16, seed=37, sample_rows=0),
+    W.PREFILL_32K.replace(name="prefill_L7000_k1024_hi48", seq_len=7000, k=1024, H_I=48, seed=38, sample_rows=0),
 ]
 
 
