@@ -184,6 +184,31 @@ def test_streaming_fallbacks_bit_exact(kind):
             assert np.array_equal(idx[r], np.arange(wl.k))
 
 
+def test_streaming_mixed_sequences():
+    """Two sequences of different lengths with different numbers of query rows
+    (positions 6000..8999 of a 9000-token sequence, 2000..6999 of a 7000-token
+    one): per-row positions, thresholds and lists across sequences."""
+    import dataclasses
+    wl = W.PREFILL_32K.replace(name="prefill_b2_L9000_mixed", seqs=2, seq_len=9000, seed=39, sample_rows=0)
+    announce("streaming prefill", wl.name, "lens 9000/7000, rows 3000/5000")
+    full = W.generate(wl, DEV)
+    sel = torch.cat([torch.arange(6000, 9000), torch.arange(9000, 14000)]).to(DEV)
+    pick = lambda t: None if t is None else t[sel].contiguous()  # noqa: E731
+    i32 = dict(dtype=torch.int32, device=DEV)
+    inp = dataclasses.replace(full, seq_lens=torch.tensor([9000, 7000], **i32),
+                              q_start=torch.tensor([0, 3000, 8000], **i32), num_rows=8000, max_q=5000, max_len=9000,
+                              seq_lens_host=[9000, 7000], q_start_host=[0, 3000, 8000], q8=pick(full.q8),
+                              q_scale=pick(full.q_scale), w=pick(full.w), q=pick(full.q))
+    p, s = _both(inp)
+    _assert_same(p, s, wl.name)
+    idx, out, lse = (to_np(x) for x in s)
+    # seq 0 rows 0..2999 (n = 6001..9000; the capacity 7168 is crossed at rows 1167/1168); seq 1 rows
+    # 3000..7999 (n = 2001..7000, all under the capacity; k = 2048 is crossed at rows 3047/3048)
+    rows = [0, 1167, 1168, 2999, 3000, 3046, 3047, 3048, 7999]
+    rows = sorted(set(rows) | set(W.sample_rows(wl, 8000, 12, always=())))
+    _oracle_check(inp, idx, out, lse, rows, exact=False)
+
+
 def test_streaming_repeatable():
     """Two calls give bit-identical results (the list order from atomics never shows)."""
     wl = CASES[1]
