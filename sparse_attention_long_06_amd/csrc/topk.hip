@@ -260,15 +260,24 @@ __global__ void __launch_bounds__(kFinalNT) topk_finalize_kernel(TopkArgs a) {
   }
 }
 
+// Clears n words; 16-byte stores for the whole quads when p is 16-byte aligned.
 __global__ void zero_u32_kernel(uint32_t* p, int64_t n) {
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
-    p[i] = 0u;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  const int64_t i0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  int64_t done = 0;
+  if ((reinterpret_cast<uintptr_t>(p) & 15) == 0) {
+    uint4* q = reinterpret_cast<uint4*>(p);
+    const int64_t nq = n >> 2;
+    for (int64_t i = i0; i < nq; i += stride) q[i] = make_uint4(0u, 0u, 0u, 0u);
+    done = nq << 2;
+  }
+  for (int64_t i = done + i0; i < n; i += stride) p[i] = 0u;
 }
 
 hipError_t launch_zero(uint32_t* p, int64_t n, hipStream_t stream) {
   if (n <= 0) return hipSuccess;
-  const int64_t want = (n + 255) / 256;
-  const int64_t blocks = want < 1024 ? want : 1024;
+  const int64_t want = (n / 4 + 255) / 256 + 1;
+  const int64_t blocks = want < 256 ? want : 256;
   hipLaunchKernelGGL(zero_u32_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, p, n);
   return hipGetLastError();
 }
