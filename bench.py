@@ -38,7 +38,7 @@ INDEXER_COUNTERS = {
     "sources": ["sparse_attention_long_06_amd/csrc/indexer.hip", "sparse_attention_long_06_amd/csrc/idx_math.h",
                 "sparse_attention_long_06_amd/csrc/dsa_common.h", "sparse_attention_long_06_amd/csrc/dsa_kernels.h",
                 "sparse_attention_long_06_amd/csrc/api.hip"],
-    "sha256": "36bb081f79ca98a016b85b7e1a0d8e0527c9fab9e07f02d6de0e2807c9de46ec",
+    "sha256": "eb4832921c7b20533dd8319a40b9b922d25ecc5485dfa22b44e56c6e2c5f09e1",
     "fetch_kib": 272619.9,
     "write_kib": 17231.0,
     "fetch_scale": 2.0,

@@ -409,6 +409,15 @@ __global__ void __launch_bounds__(256) indexer_decode_ring_kernel(IndexerArgs a)
 // keys past their own position (those entries of the score matrix are
 // unspecified), so every wave stores the same number of scores per slot and
 // the vector-memory counter the ring waits on stays exact.
+//
+// FILT (the streaming prefill selection): no score is stored.  Each wave
+// keeps, per row, the (key, token) pairs whose order (key desc, token asc)
+// reaches the row's threshold in an LDS buffer, one ballot-compacted append
+// per 64-key slot, and flushes the buffer as a segment of the row's candidate
+// list (see stream.hip).  The reservation atomic of a flush waits for every
+// older DMA of the wave, so the ring waits stay correct, only longer, when a
+// flush falls inside the loop.  kshift > 0 runs the kernel over a compacted
+// sample of every 2^kshift-th token (causal bound p >> kshift).
 constexpr int kPreRing = 6;
 constexpr int kPreKeys = 64;
 
