@@ -86,6 +86,9 @@ VARIANTS = [
     W.SMALL_PREFILL.replace(name="prefill_b2_L2300_paged64", seqs=2, seq_len=2300, paged=True, block_size=64,
                             seed=26),
     W.SMALL_PREFILL.replace(name="prefill_L2100_paged16", seq_len=2100, paged=True, block_size=16, seed=27),
+    # a wider length range than the 4K-128K paged batch: 1000 to 262144 tokens per sequence
+    W.PAGED_DECODE_MIXED.replace(name="paged_decode_b6_mixed1k_256k", seqs=6, seq_len=262144, min_len=1000,
+                                 seed=40),
 ]
 
 

@@ -184,6 +184,20 @@ def test_streaming_fallbacks_bit_exact(kind):
             assert np.array_equal(idx[r], np.arange(wl.k))
 
 
+def test_streaming_long_context_chunk():
+    """The last 320 rows of a 200000-token sequence (about 200 segments per row, 6250 sampled scores per
+    threshold)."""
+    wl = W.CHUNKED_128K.replace(name="chunked_prefill_L200000_c512", seq_len=200000, chunk=512, seed=41,
+                                sample_rows=0)
+    c = (wl.seq_len + wl.chunk - 1) // wl.chunk - 1
+    announce("streaming chunked prefill", wl.name, "chunk", c)
+    inp = W.generate(wl, DEV, chunk_index=c)
+    p, s = _both(inp)
+    _assert_same(p, s, wl.name)
+    idx, out, lse = (to_np(x) for x in s)
+    _oracle_check(inp, idx, out, lse, [0, inp.num_rows // 2, inp.num_rows - 1], exact=False)
+
+
 def test_streaming_mixed_sequences():
     """Two sequences of different lengths with different numbers of query rows
     (positions 6000..8999 of a 9000-token sequence, 2000..6999 of a 7000-token
