@@ -38,9 +38,9 @@ INDEXER_COUNTERS = {
     "sources": ["sparse_attention_long_06_amd/csrc/indexer.hip", "sparse_attention_long_06_amd/csrc/idx_math.h",
                 "sparse_attention_long_06_amd/csrc/dsa_common.h", "sparse_attention_long_06_amd/csrc/dsa_kernels.h",
                 "sparse_attention_long_06_amd/csrc/api.hip"],
-    "sha256": "eb4832921c7b20533dd8319a40b9b922d25ecc5485dfa22b44e56c6e2c5f09e1",
-    "fetch_kib": 272619.9,
-    "write_kib": 17231.0,
+    "sha256": "5fb3e49894e3840f547e4ba0aecff93237bd3439c42e88c16aef01832acfc9bd",
+    "fetch_kib": 272779.8,
+    "write_kib": 17230.3,
     "fetch_scale": 2.0,
     "write_scale": 1.0,
 }

@@ -206,8 +206,12 @@ __global__ void __launch_bounds__(256) indexer_decode_ring_kernel(IndexerArgs a)
   constexpr int DI = 128;
   constexpr int SLOT = 16 * DI + 64;          // key bytes + 16 fp32 scales
   constexpr int PER = SCALE ? 3 : 2;          // DMA instructions per tile
-  __shared__ uint32_t hist[HIST ? kBins1 : 1];
+  // The chunk's scores collect in LDS and leave in one coalesced pass after
+  // the ring has drained, so no global store shares the vector-memory counter
+  // the ring waits on; the histogram is then built in the ring's space.
+  __shared__ __attribute__((aligned(16))) float sbuf[kIdxDecodeChunk];
   __shared__ __attribute__((aligned(16))) char ring[4][kRing][SLOT];
+  static_assert(!HIST || sizeof(ring) >= kBins1 * sizeof(uint32_t), "histogram fits the ring");
 
   const int b = blockIdx.z;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -218,9 +222,6 @@ __global__ void __launch_bounds__(256) indexer_decode_ring_kernel(IndexerArgs a)
   const int kbeg = blockIdx.x * a.chunk;
   const int kend = min(kbeg + a.chunk, len);
   if (kbeg >= kend) return;                   // uniform over the workgroup
-  if constexpr (HIST) {
-    for (int i = threadIdx.x; i < kBins1; i += 256) hist[i] = 0u;
-  }
   // q_scale[b] through the scalar cache: a vector load here would make the
   // compiler wait on the vector-memory counter, which the ring DMA shares
   const float qs = a.q_scale ? *(const __attribute__((address_space(4))) float*)(uintptr_t)(a.q_scale + b) : 1.0f;
@@ -354,14 +355,7 @@ __global__ void __launch_bounds__(256) indexer_decode_ring_kernel(IndexerArgs a)
   for (int m = 0; m < my_tiles; ++m) {
     if (m + kRing - 1 < my_tiles) {
       issue(m + kRing - 1);
-      // Global stores share the vector-memory counter with the DMA.  Every
-      // earlier iteration stored one score word (its tile was full: only the
-      // last tile of a chunk can be ragged, and that one waits for zero), so
-      // after the first kRing-1 tiles, kRing-1 stores sit behind tile m too.
-      if (m >= kRing - 1)
-        wait_vmcnt<(kRing - 1) * (PER + 1)>();
-      else
-        wait_vmcnt<(kRing - 1) * PER>();
+      wait_vmcnt<(kRing - 1) * PER>();        // only this wave's DMA is in flight
     } else {
       wait_vmcnt<0>();
     }
@@ -379,16 +373,19 @@ __global__ void __launch_bounds__(256) indexer_decode_ring_kernel(IndexerArgs a)
       for (int i = 0; i < 4; ++i) part = fmaf(wq[ht][i], relu(acc[i]), part);
     }
     part = group_sum(part);                   // the four lane groups holding key nl
-    const int s = kbeg + ((wave + 4 * m) << 4) + nl;
-    if (grp == 0 && s < kend) {
-      const float sc = part * ks;
-      a.scores[(int64_t)b * a.ld + s] = sc;
-      if constexpr (HIST) atomicAdd(&hist[score_key(sc) >> (32 - kBins1Bits)], 1u);
-    }
+    if (grp == 0) sbuf[((wave + 4 * m) << 4) + nl] = part * ks;   // keys past kend are never read
   }
 
+  lds_barrier();                              // every wave's scores are in; the ring is drained
+  const int nk = kend - kbeg;
+  float* srow = a.scores + (int64_t)b * a.ld + kbeg;
+  for (int i = threadIdx.x; i < nk; i += 256) srow[i] = sbuf[i];
   if constexpr (HIST) {
-    lds_barrier();                            // the histogram is complete; score stores may still be in flight
+    uint32_t* hist = reinterpret_cast<uint32_t*>(&ring[0][0][0]);
+    for (int i = threadIdx.x; i < kBins1; i += 256) hist[i] = 0u;
+    lds_barrier();
+    for (int i = threadIdx.x; i < nk; i += 256) atomicAdd(&hist[score_key(sbuf[i]) >> (32 - kBins1Bits)], 1u);
+    lds_barrier();                            // the histogram is complete
     uint32_t* gh = a.hist + (int64_t)b * kBins1;
     for (int i = threadIdx.x; i < kBins1; i += 256) {
       const uint32_t c = hist[i];
