@@ -86,6 +86,9 @@ CASES = [
     # with k = 1024 (rank 64, capacity 3584)
     W.PREFILL_32K.replace(name="prefill_L5000_k64_hi16", seq_len=5000, k=64, H_I=16, seed=37, sample_rows=0),
     W.PREFILL_32K.replace(name="prefill_L7000_k1024_hi48", seq_len=7000, k=1024, H_I=48, seed=38, sample_rows=0),
+    # k = 1 on integer scores: one winner per row among many exact ties (rank 64, capacity 3584)
+    W.PREFILL_32K.replace(name="prefill_L5000_int_k1", seq_len=5000, k=1, seed=43, sample_rows=0,
+                          integer_indexer=True),
     # 32 indexer heads (the remaining head-tile count) behind 16-token pages (smaller than a 64-key slot)
     W.PREFILL_32K.replace(name="prefill_L8500_hi32_paged16", seq_len=8500, H_I=32, paged=True, block_size=16,
                           seed=42, sample_rows=0),
