@@ -701,22 +701,31 @@ def cpu_baseline(inp, budget_s: float):
     wl = inp.wl
     B = inp.num_rows
     a = arrays_of(inp.to("cpu"))      # host copies: input preparation, not timed
-    try:
+    threads = _oracle_threads()
+
+    def rate(budget):
+        done = 0
+        t0 = time.perf_counter()
+        while True:                   # cycle over the batch's queries until the budget is spent
+            oracle.run_rows(a, [done % B])
+            done += 1
+            if time.perf_counter() - t0 >= budget:
+                break
+        return done, time.perf_counter() - t0
+
+    done, el = rate(budget_s)
+    res = {"value": round(done / el, 4), "unit": "queries/s", "cores": int(threads), "kind": "oracle",
+           "sample": f"{done} decode queries cycling over the {B} of {wl.name} (each: indexer over "
+                     f"{wl.seq_len} tokens, top-{wl.k}, attention), fp64 NumPy, {el:.1f} s"}
+    try:                              # the same oracle on one thread, over a third of the budget
         import threadpoolctl
-        threads = max(i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()) or os.cpu_count()
+        with threadpoolctl.threadpool_limits(1):
+            d1, e1 = rate(budget_s / 3)
+        res["single_thread_value"] = round(d1 / e1, 4)
+        res["single_thread_sample"] = f"{d1} queries, {e1:.1f} s"
     except Exception:  # noqa: BLE001
-        threads = os.cpu_count()
-    done = 0
-    t0 = time.perf_counter()
-    while True:                       # cycle over the batch's queries until the budget is spent
-        oracle.run_rows(a, [done % B])
-        done += 1
-        if time.perf_counter() - t0 >= budget_s:
-            break
-    el = time.perf_counter() - t0
-    return {"value": round(done / el, 4), "unit": "queries/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{done} decode queries cycling over the {B} of {wl.name} (each: indexer over "
-                      f"{wl.seq_len} tokens, top-{wl.k}, attention), fp64 NumPy, {el:.1f} s"}
+        res["single_thread_value"] = None
+    return res
 
 
 def copy_calibration(nbytes: int):
