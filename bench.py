@@ -714,9 +714,16 @@ def cpu_baseline(inp, budget_s: float):
         return done, time.perf_counter() - t0
 
     done, el = rate(budget_s)
+    cpu_model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu_model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), None)
+    except OSError:
+        pass
     res = {"value": round(done / el, 4), "unit": "queries/s", "cores": int(threads), "kind": "oracle",
            "sample": f"{done} decode queries cycling over the {B} of {wl.name} (each: indexer over "
-                     f"{wl.seq_len} tokens, top-{wl.k}, attention), fp64 NumPy, {el:.1f} s"}
+                     f"{wl.seq_len} tokens, top-{wl.k}, attention), fp64 NumPy, {el:.1f} s",
+           "full_step_s": round(B * el / done, 3), "os_cpu_count": os.cpu_count(), "cpu_model": cpu_model}
     try:                              # the same oracle on one thread, over a third of the budget
         import threadpoolctl
         with threadpoolctl.threadpool_limits(1):
