@@ -27,6 +27,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, vendor figure
+FP8_PEAK_TFLOPS = 5000.0       # MI355X dense FP8 MFMA, vendor figure
 
 # HBM traffic of one decode-indexer launch on this workload, from rocprofv3
 # counters (FETCH_SIZE and WRITE_SIZE in KiB per dispatch, averaged over the
@@ -183,14 +184,14 @@ def decode_bytes_per_query(wl, ctx):
     return idx_keys, kv + q + out + iq
 
 
-def run_bench(args):
+def run_bench(args, workload=None, separate_calls=True, attainable=True):
     import torch
 
     import workloads as W
     import sparse_attention_long_06_amd as dsa
     from sparse_attention_long_06_amd import _lib
 
-    wl = W.BY_NAME[args.workload]
+    wl = W.BY_NAME[workload or args.workload]
     if wl.kind != "decode":
         raise SystemExit(f"bench.py times the decode path; {wl.name} is a {wl.kind} workload")
     dev = torch.device("cuda:0")
@@ -275,26 +276,29 @@ def run_bench(args):
 
     # The three entry points called one by one through the binding (after the
     # timed steps), for reference next to the in-step stage times above.
-    print("[bench] per-stage calls", file=sys.stderr, flush=True)
-    scores = torch.empty((B, (inp.max_len + 3) // 4 * 4), dtype=torch.float32, device=dev)
+    st_ix = st_tk = st_at = None
+    if separate_calls:
+        print("[bench] per-stage calls", file=sys.stderr, flush=True)
+        scores = torch.empty((B, (inp.max_len + 3) // 4 * 4), dtype=torch.float32, device=dev)
 
-    def timed(fn, reps=10):
-        fn()
-        torch.cuda.synchronize()
-        ts = []
-        for _ in range(reps):
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record()
+        def timed(fn, reps=10):
             fn()
-            e1.record()
-            e1.synchronize()
-            ts.append(e0.elapsed_time(e1))
-        return sorted(ts)[len(ts) // 2]
+            torch.cuda.synchronize()
+            ts = []
+            for _ in range(reps):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                fn()
+                e1.record()
+                e1.synchronize()
+                ts.append(e0.elapsed_time(e1))
+            return sorted(ts)[len(ts) // 2]
 
-    st_ix = timed(lambda: dsa.indexer(batch, inp.q8, inp.q_scale, inp.w, inp.k8, inp.k_scale, scores=scores))
-    st_tk = timed(lambda: dsa.topk(batch, scores, wl.k, idx=idx))
-    st_at = timed(lambda: dsa.sparse_attn(batch, inp.q, inp.kv, inp.v, wl.scale, idx, out=out, lse=lse, D_v=wl.D_v))
-    del scores
+        st_ix = timed(lambda: dsa.indexer(batch, inp.q8, inp.q_scale, inp.w, inp.k8, inp.k_scale, scores=scores))
+        st_tk = timed(lambda: dsa.topk(batch, scores, wl.k, idx=idx))
+        st_at = timed(lambda: dsa.sparse_attn(batch, inp.q, inp.kv, inp.v, wl.scale, idx, out=out, lse=lse,
+                                              D_v=wl.D_v))
+        del scores
 
     ms = elapsed * 1e3 / args.steps
     qps = B / (elapsed / args.steps)
@@ -330,19 +334,27 @@ def run_bench(args):
                      "bytes_per_launch": idx_bytes, "launch_ms": round(stage_ms["indexer"], 4)},
         "stages_ms": {k: round(v, 4) for k, v in stage_ms.items()},
         "ms_per_step_with_stage_events": round(staged_ms, 4),
-        "stages_separate_calls_ms": {"indexer": round(st_ix, 4), "topk": round(st_tk, 4),
-                                     "attention": round(st_at, 4)},
+        "stages_separate_calls_ms": None if st_ix is None else {
+            "indexer": round(st_ix, 4), "topk": round(st_tk, 4), "attention": round(st_at, 4)},
         "step_hbm": {"bytes": idx_bytes + other_bytes, "GB/s": round(step_gbs, 1),
                      "frac": round(step_gbs / HBM_PEAK_GBS, 4)},
         "indexer_tflops": round(idx_flops / (stage_ms["indexer"] * 1e-3) / 1e12, 2),
+        # the decode indexer moves 132 B per 16384 FLOP (124 FLOP/B): at 8 TB/s it
+        # can reach at most 0.99 PFLOP/s, about 0.2 of the FP8 matrix-core peak
+        "indexer_tflops_frac": {"fp8_peak": round(idx_flops / (stage_ms["indexer"] * 1e-3) / 1e12 / FP8_PEAK_TFLOPS, 4),
+                                "hbm_bound_max": round(idx_flops / (stage_ms["indexer"] * 1e-3) / 1e12
+                                                       / (HBM_PEAK_GBS * 1e9 * 2 * wl.H_I * wl.d_I
+                                                          / (wl.d_I + 4) / 1e12), 4)},
         "attention": {"GB/s": round(att_gbs, 1), "hbm_frac": round(att_gbs / HBM_PEAK_GBS, 4),
                       "TFLOP/s": round(att_flops / (stage_ms["attention"] * 1e-3) / 1e12, 2),
                       "bf16_frac": round(att_flops / (stage_ms["attention"] * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)},
     }
-    del ws, out, lse
-    att = attainable_peaks()
-    res["attainable"] = att
-    res["roofline"]["frac_of_attainable"] = round(idx_gbs / att["hbm_GB/s"], 4)
+    del ws, out, lse, sets, batches
+    torch.cuda.empty_cache()
+    if attainable:
+        att = attainable_peaks()
+        res["attainable"] = att
+        res["roofline"]["frac_of_attainable"] = round(idx_gbs / att["hbm_GB/s"], 4)
     return res, inp
 
 
@@ -378,7 +390,7 @@ def _prefill_streaming_call(dsa, wl, inp, batch, out, lse, idx, ws):
                                          D_v=wl.D_v)
 
 
-def run_prefill(args):
+def run_prefill(args, attainable=True):
     """One step = indexer, top-k and sparse attention over every row of a causal
     prefill: the three entry points in turn (--select staged, the score matrix
     in HBM between them) or one dsa_prefill_streaming call (--select
@@ -464,7 +476,7 @@ def run_prefill(args):
                     "bf16_peak_frac": round(idx_tf / BF16_PEAK_TFLOPS, 4)},
         "attention": {"selected_rows": att_rows, "TFLOP/s": round(att_tf, 1),
                       "bf16_peak_frac": round(att_tf / BF16_PEAK_TFLOPS, 4)},
-        "attainable": attainable_peaks(),
+        "attainable": attainable_peaks() if attainable else None,
         "cpu_baseline": None,
     }
 
@@ -552,7 +564,8 @@ def run_chunked(args, wl):
                    "selection": args.select, "parallelism": "single GPU"},
         "stages_ms": {k: round(v, 3) for k, v in st.items()},
         "memory": {("workspace_bytes" if args.select == "streaming" else "score_matrix_bytes"): peak_ws},
-        "indexer": {"causal_pairs": pairs, "TFLOP/s": round(idx_tf, 1), "bf16_peak_frac": round(idx_tf / BF16_PEAK_TFLOPS, 4)},
+        "indexer": {"causal_pairs": pairs, "TFLOP/s": round(idx_tf, 1), "fp8_peak_frac": round(idx_tf / FP8_PEAK_TFLOPS, 4),
+                    "bf16_peak_frac": round(idx_tf / BF16_PEAK_TFLOPS, 4)},
         "attention": {"selected_rows": att_rows, "TFLOP/s": round(att_tf, 1),
                       "bf16_peak_frac": round(att_tf / BF16_PEAK_TFLOPS, 4)},
         "cpu_baseline": None,
@@ -754,6 +767,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="decode_b32_ctx128k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="decode headline only: skip the paged-decode and 32K-prefill lines of the default run")
     ap.add_argument("--select", choices=("staged", "streaming"), default="streaming",
                     help="prefill workloads: staged entry points with the score matrix, or dsa_prefill_streaming")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
@@ -775,12 +790,36 @@ def main():
         print(json.dumps(run_prefill(args)), flush=True)
         return
     res, inp = run_bench(args)
+    if not args.no_extras and args.workload == "decode_b32_ctx128k":
+        res["other_workloads"] = other_workloads(args)
     if not args.no_cpu_baseline:
         print("[bench] cpu oracle baseline", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(inp, args.cpu_budget)
     else:
         res["cpu_baseline"] = None
     print(json.dumps(res), flush=True)
+
+
+def other_workloads(args):
+    """The mixed-length paged decode and the 32K streaming prefill, timed in the
+    same run as the headline (their own roofline fractions beside it)."""
+    out = {}
+    print("[bench] paged_decode_b128_mixed4k_128k", file=sys.stderr, flush=True)
+    r, _ = run_bench(args, workload="paged_decode_b128_mixed4k_128k", separate_calls=False, attainable=False)
+    out["paged_decode_b128_mixed4k_128k"] = {
+        "metric": "queries/s", "value": r["value"], "ms_per_step": r["ms_per_step"], "steps": r["steps"],
+        "stages_ms": r["stages_ms"], "step_hbm": r["step_hbm"],
+        "indexer": {"GB/s": r["roofline"]["achieved"], "hbm_frac": r["roofline"]["frac"],
+                    "bytes_per_launch": r["roofline"]["bytes_per_launch"]},
+        "attention": r["attention"]}
+    print("[bench] prefill_L32k (streaming selection)", file=sys.stderr, flush=True)
+    pargs = argparse.Namespace(**vars(args))
+    pargs.workload, pargs.select = "prefill_L32k", "streaming"
+    pargs.steps, pargs.warmup = min(args.steps, 5), min(args.warmup, 2)
+    p = run_prefill(pargs, attainable=False)
+    out["prefill_L32k"] = {k: p[k] for k in ("metric", "value", "unit", "ms_per_step", "steps", "stages_ms",
+                                             "indexer", "attention", "memory")}
+    return out
 
 
 if __name__ == "__main__":

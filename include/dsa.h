@@ -257,6 +257,20 @@ dsa_status dsa_indexer_warmup(const dsa_batch* batch, const uint16_t* q, const d
                               float* loss, float* dq, float* dw, float* dk,
                               void* workspace, size_t ws_bytes, void* stream);
 
+/*
+ * dsa_set_attn_splits — tuning and testing hook for the attention stage of the
+ * calls that follow on this thread (dsa_sparse_attn, dsa_decode, dsa_prefill,
+ * dsa_prefill_streaming, and dsa_workspace_size for them): the k selected
+ * slots of each query row are divided among `nsplit` workgroups whose
+ * partial softmax results are merged by their log-sum-exp (the split-K form
+ * of the online softmax).  0 restores the automatic choice.  A count above
+ * what the slots allow is clamped (at most one split per 64 slots).  The
+ * result equals the unsplit one up to the rounding of the partials; set the
+ * same value before sizing and before calling.
+ * Errors: DSA_ERR_SHAPE if nsplit is outside [0, 4096].
+ */
+dsa_status dsa_set_attn_splits(int nsplit);
+
 /* Which call dsa_workspace_size() sizes. */
 enum { DSA_WS_TOPK = 1, DSA_WS_ATTN = 2, DSA_WS_DECODE = 3, DSA_WS_PREFILL = 4, DSA_WS_WARMUP = 5,
        DSA_WS_PREFILL_STREAM = 6 };

@@ -105,7 +105,7 @@ def token_rows(cache: np.ndarray, seq: int, n: int, block_table=None, block_size
 
 
 def indexer_scores(q8: np.ndarray, q_scale: float, w: np.ndarray, k8: np.ndarray,
-                   k_scale) -> np.ndarray:
+                   k_scale, with_abs: bool = False):
     """Scores of n cached tokens for one query row.
 
     q8 [H_I, d_I] e4m3fn codes, q_scale scalar (None = 1), w [H_I] head weights,
@@ -113,15 +113,25 @@ def indexer_scores(q8: np.ndarray, q_scale: float, w: np.ndarray, k8: np.ndarray
         I[s] = sum_j w[j] * q_scale * k_scale[s] * max(sum_d q[j,d] k[s,d], 0)
     The fp64 dot products are exact: each e4m3fn product is a multiple of
     2^-18 below 2^18, so a 128-term sum needs fewer than 53 bits.
+    With ``with_abs`` also returns the absolute-term sum of every score,
+        A[s] = sum_j |w[j] * q_scale| * k_scale[s] * max(z[j,s], 0),
+    the scale against which a score's rounding error is judged.
     """
-    q = decode_e4m3fn(q8)                              # [H_I, d_I]
-    k = decode_e4m3fn(k8)                              # [n, d_I]
+    return indexer_scores_values(decode_e4m3fn(q8), q_scale, w, decode_e4m3fn(k8), k_scale, with_abs)
+
+
+def indexer_scores_values(q: np.ndarray, q_scale, w: np.ndarray, k: np.ndarray, k_scale,
+                          with_abs: bool = False):
+    """indexer_scores on already decoded FP8 values (q [H_I, d_I], k [n, d_I] float64)."""
     z = q @ k.T                                        # [H_I, n] logits per indexer head
     relu = np.maximum(z, 0.0)
     qs = 1.0 if q_scale is None else float(q_scale)
     ks = np.ones(k.shape[0]) if k_scale is None else np.asarray(k_scale, dtype=np.float64)
     wj = np.asarray(w, dtype=np.float64) * qs          # [H_I]
-    return (wj @ relu) * ks
+    scores = (wj @ relu) * ks
+    if not with_abs:
+        return scores
+    return scores, (np.abs(wj) @ relu) * ks
 
 
 # --------------------------------------------------------------------------
@@ -215,14 +225,16 @@ def run_rows(a: dict, rows, select_dtype=np.float32, need=("scores", "idx", "out
     block_table, block_size, k, scale.
 
     Returns a dict of per-row lists: scores (float64 [n]), idx (int32 [k]),
-    out (float64 [H, D_v]), lse (float64 [H]).  ``idx_override`` maps a row to
+    out (float64 [H, D_v]), lse (float64 [H]), and with "abs" in ``need`` the
+    absolute-term sums of the scores (see indexer_scores).  ``idx_override`` maps a row to
     an index set to attend over instead of the oracle's own selection.
     """
+    rows = list(rows)
     geo = row_geometry(a["seq_lens"], a.get("q_start"), a["q8"].shape[0])
     table = a.get("block_table")
     bs = int(a.get("block_size") or 0)
     k = int(a["k"])
-    res = {"scores": [], "idx": [], "out": [], "lse": []}
+    res = {"scores": [], "abs": [], "idx": [], "out": [], "lse": []}
 
     def att_rows(name, b, n, sel):
         """Rows `sel` (logical token indices) of sequence b's cache `name`, as float64."""
@@ -232,13 +244,24 @@ def run_rows(a: dict, rows, select_dtype=np.float32, need=("scores", "idx", "out
             return None
         return decode_bf16(token_rows(a[name], b, n, table, bs)[sel])
 
+    keys = {}                     # sequence -> decoded index keys of its longest requested prefix
+
+    def key_values(b, n):
+        if b not in keys or keys[b].shape[0] < n:
+            longest = max(p + 1 for (bb, p) in (geo[r] for r in rows) if bb == b)
+            keys[b] = decode_e4m3fn(token_rows(a["k8"], b, longest, table, bs))
+        return keys[b][:n]
+
     for t in rows:
         b, p = geo[t]
         n = p + 1
-        k8 = token_rows(a["k8"], b, n, table, bs)
         ks = None if a.get("k_scale") is None else token_rows(a["k_scale"], b, n, table, bs)
         qs = None if a.get("q_scale") is None else a["q_scale"][t]
-        sc = indexer_scores(a["q8"][t], qs, a["w"][t], k8, ks)
+        sc = indexer_scores_values(decode_e4m3fn(a["q8"][t]), qs, a["w"][t], key_values(b, n), ks,
+                                   with_abs="abs" in need)
+        if "abs" in need:
+            sc, ab = sc
+            res["abs"].append(ab)
         res["scores"].append(sc)
         sel_scores = sc.astype(select_dtype) if select_dtype is not None else sc
         idx = topk_indices(sel_scores, k)

@@ -26,7 +26,7 @@ from ._lib import (DSA_WS_ATTN, DSA_WS_DECODE, DSA_WS_PREFILL, DSA_WS_PREFILL_ST
                    DSA_WS_TOPK, DSA_WS_WARMUP, DsaBatch, DsaCache)
 
 __all__ = ["Batch", "DsaError", "indexer", "topk", "sparse_attn", "decode", "prefill", "prefill_streaming",
-           "indexer_warmup", "workspace_size", "cache_view"]
+           "indexer_warmup", "workspace_size", "cache_view", "set_attn_splits"]
 
 
 class DsaError(RuntimeError):
@@ -101,6 +101,11 @@ def cache_view(t: Optional[torch.Tensor], batch: Batch) -> Optional[DsaCache]:
 
 def _ref(c):
     return None if c is None else ctypes.byref(c)
+
+
+def set_attn_splits(nsplit: int) -> None:
+    """dsa_set_attn_splits: force the attention split count of later calls on this thread (0 = automatic)."""
+    _check(_lib.load().dsa_set_attn_splits(int(nsplit)), "dsa_set_attn_splits")
 
 
 def workspace_size(entry: int, batch: Batch, k: int, H: int = 0, D_v: int = 0) -> int:

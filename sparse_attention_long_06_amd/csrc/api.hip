@@ -19,6 +19,7 @@ constexpr int kMaxStageEvents = 6;
 thread_local hipEvent_t g_stage_events[kMaxStageEvents] = {};
 thread_local int g_stage_count = 0;
 thread_local bool g_stage_armed = false;
+thread_local int g_force_splits = 0;   // dsa_set_attn_splits: 0 = the planner's choice
 
 dsa_status fail(dsa_status s, const char* fmt, ...) {
   char buf[512];
@@ -150,7 +151,9 @@ AttnPlan plan_attn(int T, int k, int H, int D_v) {
   AttnPlan p;
   const int blocks = (k + kAttnBlock - 1) / kAttnBlock;
   int ns = 1;
-  if (T > 0 && T < 256) {
+  if (g_force_splits > 0) {
+    ns = g_force_splits < blocks ? g_force_splits : blocks;
+  } else if (T > 0 && T < 256) {
     while (ns < blocks && (int64_t)T * ns < 256) ns *= 2;
     if (ns > blocks) ns = blocks;
   }
@@ -403,9 +406,19 @@ dsa_status check_attn_args(const dsa_batch* b, const uint16_t* q, const dsa_cach
 
 }  // namespace
 
+// Records `msg` as this thread's last error and returns `s` (for the other
+// source files of the library).
+dsa_status dsa_record_error(dsa_status s, const char* msg) { return fail(s, "%s", msg); }
+
 // ====================================================================== C ABI
 
 extern "C" const char* dsa_last_error(void) { return g_err.c_str(); }
+
+extern "C" dsa_status dsa_set_attn_splits(int nsplit) {
+  CHECK(nsplit >= 0 && nsplit <= 4096, DSA_ERR_SHAPE, "nsplit %d outside [0, 4096]", nsplit);
+  g_force_splits = nsplit;
+  return ok();
+}
 
 extern "C" dsa_status dsa_set_stage_events(void* const* events, int count) {
   if (!events) {

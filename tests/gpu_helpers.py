@@ -37,9 +37,7 @@ def gpu_staged(inp):
 
 def oracle_abs_terms(a, rows):
     """sum_j |w_j| q_scale k_scale ReLU(z_j) per candidate: the scale of the score's rounding error."""
-    b = dict(a)
-    b["w"] = np.abs(a["w"])
-    return oracle.run_rows(b, rows, need=("scores",))["scores"]
+    return oracle.run_rows(a, rows, need=("scores", "abs"))["abs"]
 
 
 def check_scores(gpu_scores, ref, absterms, rows, exact=False):
@@ -81,3 +79,45 @@ def to_np(t):
     if t.dtype == torch.bfloat16:
         return t.float().numpy()
     return t.numpy()
+
+
+def oracle_rows(a, rows, need=("scores", "abs", "idx", "out"), idx_override=None, workers=16, per_task=8):
+    """oracle.run_rows over ``rows``, in tasks of ``per_task`` rows on a thread pool.
+
+    The oracle's heavy steps (matrix products, sorts, elementwise passes over
+    large arrays) run inside numpy with the GIL released, so threads overlap;
+    BLAS is held to one thread per worker.  The result is the one run_rows
+    gives for the same rows in one call (the same function on each task)."""
+    from concurrent.futures import ThreadPoolExecutor
+    import threadpoolctl
+
+    rows = list(rows)
+    tasks = [rows[i: i + per_task] for i in range(0, len(rows), per_task)]
+    with threadpoolctl.threadpool_limits(1), ThreadPoolExecutor(max(1, min(workers, len(tasks)))) as ex:
+        parts = list(ex.map(lambda rs: oracle.run_rows(a, rs, need=need, idx_override=idx_override), tasks))
+    return {key: [x for p in parts for x in p[key]] for key in parts[0]} if parts else \
+        {"scores": [], "abs": [], "idx": [], "out": [], "lse": []}
+
+
+def check_rows(a, rows, g_idx, g_out, g_lse, ref, k, what, min_same=0.9):
+    """The selection rule on every row and the attention check on every row.
+
+    g_idx/g_out/g_lse hold the GPU's results for ``rows`` in the same order.
+    Where the GPU selected the oracle's set, its attention is compared with the
+    oracle's end-to-end output; where a near-tie swap made the sets differ,
+    with the oracle's attention over the GPU's own set.  Returns the number of
+    rows whose sets agree; at least ``min_same`` of the rows must."""
+    same, differ = 0, {}
+    for i, r in enumerate(rows):
+        if check_topk_swaps(g_idx[i], ref["idx"][i], ref["scores"][i], k):
+            same += 1
+            check_attention(g_out[i], g_lse[i], ref["out"][i], ref["lse"][i], f"{what} row {r}")
+        else:
+            differ[r] = i
+    if differ:
+        own = oracle_rows(a, list(differ), need=("scores", "idx", "out"),
+                          idx_override={r: np.asarray(g_idx[i]) for r, i in differ.items()})
+        for j, (r, i) in enumerate(differ.items()):
+            check_attention(g_out[i], g_lse[i], own["out"][j], own["lse"][j], f"{what} row {r} (GPU's own set)")
+    assert same >= min_same * len(rows), f"{what}: only {same}/{len(rows)} rows selected the same set"
+    return same

@@ -1,16 +1,19 @@
 """GPU parity at the workloads' full sizes, in the launch configuration the benchmark times.
 
-The oracle recomputes sampled rows one by one on the host:
+The oracle recomputes rows one by one on the host (tests/gpu_helpers.oracle_rows):
   * 128K batched decode (32 queries) and mixed-length paged decode (128
-    queries): every query, through the fused dsa_decode entry point, plus the
-    indexer scores of a few rows through dsa_indexer;
+    queries): every query through the fused dsa_decode entry point, and the
+    indexer scores of every query through dsa_indexer;
   * 32K prefill: 512 seeded rows, always including the first rows, the rows
     around the k = 2048 boundary and the last row;
-  * 128K chunked prefill: every chunk runs; sampled rows of a spread of chunks
-    (first and last row of each sampled chunk included) are checked.
-The prefill workloads also run dsa_prefill_streaming (the configuration the
-benchmark times for them), whose selection, output and lse must equal the
-staged calls' bit for bit on every row of every chunk.
+  * 128K chunked prefill: 256 seeded rows of every one of the 32 chunks, always
+    including each chunk's first and last row.
+Every checked row gets the score rule, the selection rule and an attention
+check (against the oracle's own set, or, after a near-tie swap, against the
+oracle's attention over the GPU's set).  The prefill workloads also run
+dsa_prefill_streaming (the configuration the benchmark times for them), whose
+selection, output and lse must equal the staged calls' bit for bit on every
+row of every chunk.
 Rules as in test_gpu_parity.py.
 """
 import time
@@ -19,27 +22,15 @@ import numpy as np
 import pytest
 import torch
 
-import oracle
 import workloads as W
 import sparse_attention_long_06_amd as dsa
-from tests.gpu_helpers import (DEV, announce, arrays_of, check_attention, check_scores, check_topk_swaps,
-                               oracle_abs_terms, to_np)
+from tests.gpu_helpers import DEV, announce, arrays_of, check_rows, check_scores, oracle_rows, to_np
 
 pytestmark = pytest.mark.gpu
 
 
 def _log(*a):
     print("[fullsize]", *a, flush=True)
-
-
-def _check_rows(ref, rows, idx, out, lse, k, min_same=0.9, what=""):
-    same = 0
-    for i, r in enumerate(rows):
-        if check_topk_swaps(idx[r], ref["idx"][i], ref["scores"][i], k):
-            same += 1
-            check_attention(out[r], lse[r], ref["out"][i], ref["lse"][i], f"{what} row {r}")
-    assert same >= min_same * len(rows), f"{what}: only {same}/{len(rows)} rows selected the same set"
-    return same
 
 
 def _streaming_equals(inp, batch, idx, out, lse, what):
@@ -71,11 +62,10 @@ def test_decode_fullsize_all_queries(wl):
     g_idx, g_out, g_lse, g_sc = to_np(idx), to_np(out), to_np(lse), to_np(scores)
     a = arrays_of(inp)
     rows = list(range(inp.num_rows))
-    ref = oracle.run_rows(a, rows)
+    ref = oracle_rows(a, rows, per_task=2)
     _log(wl.name, "oracle done", f"{time.time() - t0:.1f}s")
-    score_rows = rows[:: max(1, len(rows) // 6)]
-    check_scores(g_sc, [ref["scores"][r] for r in score_rows], oracle_abs_terms(a, score_rows), score_rows)
-    same = _check_rows(ref, rows, g_idx, g_out, g_lse, wl.k, what=wl.name)
+    check_scores(g_sc, ref["scores"], ref["abs"], rows)
+    same = check_rows(a, rows, g_idx, g_out, g_lse, ref, wl.k, wl.name)
     _log(wl.name, f"{same}/{len(rows)} identical selections", f"{time.time() - t0:.1f}s")
 
 
@@ -92,31 +82,44 @@ def test_prefill_32k_sampled_rows():
     _log(wl.name, "gpu done", f"{time.time() - t0:.1f}s")
     rows = W.sample_rows(wl, inp.num_rows, wl.sample_rows, always=(0, 1, 2046, 2047, 2048, 2049, 32767))
     rows_t = torch.tensor(rows, device=DEV)
-    g_idx = to_np(idx[rows_t])
-    g_out = to_np(out[rows_t])
-    g_lse = to_np(lse[rows_t])
-    g_sc = to_np(scores[rows_t])
+    g_idx, g_out, g_lse, g_sc = (to_np(x[rows_t]) for x in (idx, out, lse, scores))
     del scores, out
     a = arrays_of(inp)
-    ref = oracle.run_rows(a, rows)
+    ref = oracle_rows(a, rows)
     _log(wl.name, "oracle done", f"{time.time() - t0:.1f}s")
-    local = list(range(len(rows)))
-    check_scores(g_sc, ref["scores"], oracle_abs_terms(a, rows), local)
-    same = _check_rows(ref, local, g_idx, g_out, g_lse, wl.k, what=wl.name)
+    check_scores(g_sc, ref["scores"], ref["abs"], list(range(len(rows))))
+    same = check_rows(a, rows, g_idx, g_out, g_lse, ref, wl.k, wl.name)
     for i, r in enumerate(rows):       # rows with t < k select every prior token
         if r < wl.k:
             assert g_idx[i][: r + 1].tolist() == list(range(r + 1))
     _log(wl.name, f"{same}/{len(rows)} identical selections", f"{time.time() - t0:.1f}s")
 
 
-def test_chunked_prefill_128k_sampled_chunks():
+# ------------------------------------------------------------------ 128K chunked prefill, every chunk
+
+CHUNK_GROUPS = 8
+
+
+def _sparse_rows(shape, dtype, rows, values):
+    """A [num_rows, ...] host array holding ``values`` at ``rows`` (other rows are never read)."""
+    out = np.zeros(shape, dtype=dtype)      # untouched pages stay unallocated
+    out[rows] = values
+    return out
+
+
+@pytest.fixture(scope="module")
+def chunked_128k():
+    """Every chunk of the 128K chunked prefill on the GPU (staged entry points and
+    the streaming one, which must agree bit for bit), keeping the sampled rows'
+    results and query-side inputs on the host for the oracle."""
     wl = W.CHUNKED_128K
-    announce("full-size chunked prefill", wl.name)
+    announce("full-size chunked prefill (GPU pass over all chunks)", wl.name)
     t0 = time.time()
     nchunks = wl.seq_len // wl.chunk
-    check_chunks = {0, 1, nchunks // 2, nchunks - 1}
     first = W.generate(wl, DEV, chunk_index=0)
     cache = W.cache_of(first)
+    host_cache = {k: v for k, v in arrays_of(first).items() if k in ("k8", "k_scale", "kv", "v")}
+    chunks = []
     for c in range(nchunks):
         inp = first if c == 0 else W.generate(wl, DEV, chunk_index=c, cache=cache)
         batch = dsa.Batch.from_inputs(inp)
@@ -124,14 +127,35 @@ def test_chunked_prefill_128k_sampled_chunks():
         idx = dsa.topk(batch, scores, wl.k)
         out, lse = dsa.sparse_attn(batch, inp.q, inp.kv, inp.v, wl.scale, idx, D_v=wl.D_v)
         _streaming_equals(inp, batch, idx, out, lse, f"chunk {c}")
-        if c not in check_chunks:
-            continue
         rows = W.sample_rows(wl, inp.num_rows, wl.sample_rows, always=(0, inp.num_rows - 1))
         rows_t = torch.tensor(rows, device=DEV)
-        g_idx, g_out, g_lse, g_sc = (to_np(x[rows_t]) for x in (idx, out, lse, scores))
-        a = arrays_of(inp)
-        ref = oracle.run_rows(a, rows)
-        local = list(range(len(rows)))
-        check_scores(g_sc, ref["scores"], oracle_abs_terms(a, rows), local)
-        same = _check_rows(ref, local, g_idx, g_out, g_lse, wl.k, what=f"chunk {c}")
+        g = {name: to_np(x[rows_t]) for name, x in (("idx", idx), ("out", out), ("lse", lse), ("scores", scores))}
+        T = inp.num_rows
+        q8 = to_np(inp.q8[rows_t])
+        q = inp.q[rows_t].cpu().view(torch.int16).numpy().view(np.uint16)
+        a = dict(host_cache, q8=_sparse_rows((T,) + q8.shape[1:], np.uint8, rows, q8),
+                 q_scale=_sparse_rows((T,), np.float32, rows, to_np(inp.q_scale[rows_t])),
+                 w=_sparse_rows((T, wl.H_I), np.float32, rows, to_np(inp.w[rows_t])),
+                 q=_sparse_rows((T,) + q.shape[1:], np.uint16, rows, q),
+                 seq_lens=list(inp.seq_lens_host), q_start=inp.q_start_host, block_table=None, block_size=0,
+                 k=wl.k, scale=wl.scale, D_v=wl.D_v)
+        chunks.append(dict(rows=rows, a=a, g=g))
+        del scores, idx, out, lse, inp, batch
+        if c % 8 == 7:
+            _log(wl.name, f"gpu chunks 0-{c} done", f"{time.time() - t0:.1f}s")
+    torch.cuda.empty_cache()
+    return chunks
+
+
+@pytest.mark.parametrize("group", range(CHUNK_GROUPS))
+def test_chunked_prefill_128k_every_chunk(chunked_128k, group):
+    wl = W.CHUNKED_128K
+    per = len(chunked_128k) // CHUNK_GROUPS
+    t0 = time.time()
+    for c in range(group * per, (group + 1) * per):
+        ch = chunked_128k[c]
+        rows, a, g = ch["rows"], ch["a"], ch["g"]
+        ref = oracle_rows(a, rows)
+        check_scores(g["scores"], ref["scores"], ref["abs"], list(range(len(rows))))
+        same = check_rows(a, rows, g["idx"], g["out"], g["lse"], ref, wl.k, f"chunk {c}")
         _log(wl.name, f"chunk {c}: {same}/{len(rows)} identical selections", f"{time.time() - t0:.1f}s")

@@ -17,7 +17,8 @@ import torch
 import oracle
 import workloads as W
 import sparse_attention_long_06_amd as dsa
-from tests.gpu_helpers import (DEV, announce, arrays_of, check_attention, check_topk_swaps, to_np)
+from tests.gpu_helpers import (DEV, announce, arrays_of, check_attention, check_rows, check_topk_swaps,
+                               oracle_rows, to_np)
 
 pytestmark = pytest.mark.gpu
 
@@ -56,17 +57,12 @@ def _assert_same(p, s, what):
 
 def _oracle_check(inp, idx, out, lse, rows, exact):
     a = arrays_of(inp)
-    ref = oracle.run_rows(a, rows)
-    same = 0
-    for i, r in enumerate(rows):
-        if exact:
+    ref = oracle_rows(a, rows, need=("scores", "idx", "out"))
+    if exact:
+        for i, r in enumerate(rows):
             assert np.array_equal(idx[r], ref["idx"][i]), f"row {r}: selection not exact"
-            same += 1
-            check_attention(out[r], lse[r], ref["out"][i], ref["lse"][i], f"row {r}")
-        elif check_topk_swaps(idx[r], ref["idx"][i], ref["scores"][i], inp.wl.k):
-            same += 1
-            check_attention(out[r], lse[r], ref["out"][i], ref["lse"][i], f"row {r}")
-    assert same >= 0.9 * len(rows), f"only {same}/{len(rows)} rows selected the same set"
+    check_rows(a, rows, idx[rows], out[rows], lse[rows], ref, inp.wl.k, inp.wl.name,
+               min_same=1.0 if exact else 0.9)
     return ref
 
 

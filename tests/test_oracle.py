@@ -344,3 +344,18 @@ def test_row_geometry():
     assert oracle.row_geometry([3], [0, 3], 3) == [(0, 0), (0, 1), (0, 2)]
     # a chunk of 2 query rows at the end of a 6-token cache
     assert oracle.row_geometry([6], [0, 2], 2) == [(0, 4), (0, 5)]
+
+
+def test_abs_terms_are_scores_with_absolute_weights():
+    # the absolute-term sum (the tolerance scale of a score) is the score the
+    # same row would get with every head weight replaced by its magnitude
+    rng = np.random.default_rng(12)
+    H_I, d_I, n = 5, 16, 40
+    q8 = _finite_codes(rng, (H_I, d_I))
+    k8 = _finite_codes(rng, (n, d_I))
+    w = rng.normal(size=H_I).astype(np.float32)
+    ks = rng.uniform(0.1, 2.0, size=n).astype(np.float32)
+    sc, ab = oracle.indexer_scores(q8, 0.7, w, k8, ks, with_abs=True)
+    assert np.array_equal(sc, oracle.indexer_scores(q8, 0.7, w, k8, ks))
+    assert np.allclose(ab, oracle.indexer_scores(q8, 0.7, np.abs(w), k8, ks), rtol=1e-15, atol=0)
+    assert (ab >= np.abs(sc) - 1e-12 * ab).all()
