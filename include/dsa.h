@@ -271,6 +271,31 @@ dsa_status dsa_indexer_warmup(const dsa_batch* batch, const uint16_t* q, const d
  */
 dsa_status dsa_set_attn_splits(int nsplit);
 
+/*
+ * dsa_decode_noalloc — dsa_decode for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc.  Arguments, results and errors as dsa_decode, without
+ * the workspace: it uses a static device array of
+ * dsa_noalloc_scratch_bytes() bytes (256 MiB) instead, one per GPU, held
+ * from the library's first use of that GPU until the process ends.  The
+ * first call on a device looks the array up (hipGetSymbolAddress, with that
+ * device current); no call allocates or frees memory.
+ *   DSA_ERR_WORKSPACE when dsa_workspace_size(DSA_WS_DECODE, ...) for the
+ *   batch exceeds the array (use dsa_decode with a caller workspace then).
+ * All calls on one GPU share its array, which keeps the last call's contents
+ * (everything that must start at zero is cleared by each call): calls that
+ * overlap on one GPU (other streams, other threads) race and must be
+ * serialised by the caller.
+ */
+dsa_status dsa_decode_noalloc(const dsa_batch* batch, const uint8_t* q8, const float* q_scale,
+                              const float* w, const dsa_cache* kidx, const dsa_cache* kscale,
+                              int H_I, int d_I, int k, const uint16_t* q, const dsa_cache* kv,
+                              const dsa_cache* v, int H, int D, int D_v, float scale,
+                              uint16_t* out, float* lse, int32_t* idx_out, void* stream);
+
+/* Size in bytes of dsa_decode_noalloc's static scratch array (host-only). */
+size_t dsa_noalloc_scratch_bytes(void);
+
 /* Which call dsa_workspace_size() sizes. */
 enum { DSA_WS_TOPK = 1, DSA_WS_ATTN = 2, DSA_WS_DECODE = 3, DSA_WS_PREFILL = 4, DSA_WS_WARMUP = 5,
        DSA_WS_PREFILL_STREAM = 6 };

@@ -43,6 +43,9 @@ SIGNATURES = {
                                _SZ, _P], _I),
     "dsa_indexer_warmup": ([_BP, _P, _CP, _I, _I, _F, _P, _P, _P, _CP, _CP, _I, _I, _P, _P, _P, _P, _P, _SZ, _P],
                            _I),
+    "dsa_decode_noalloc": ([_BP, _P, _P, _P, _CP, _CP, _I, _I, _I, _P, _CP, _CP, _I, _I, _I, _F, _P, _P, _P, _P],
+                           _I),
+    "dsa_noalloc_scratch_bytes": ([], _SZ),
     "dsa_workspace_size": ([_I, _BP, _I, _I, _I], _SZ),
     "dsa_set_stage_events": ([ctypes.POINTER(ctypes.c_void_p), _I], _I),
     "dsa_set_attn_splits": ([_I], _I),

@@ -287,3 +287,17 @@ def test_probe_sizes_and_argument_checks(probes):
     assert probes.dsa_probe_mfma(2, 10, FAKE, big, None) == -1
     assert probes.dsa_probe_mfma(0, 0, FAKE, big, None) == -1
     assert probes.dsa_probe_mfma(1, 10, FAKE, probes.dsa_probe_mfma_sink_words() - 1, None) == -1
+
+
+def test_noalloc_rejects_batches_beyond_its_scratch(lib):
+    # the size check happens on the host before any device call
+    assert lib.dsa_noalloc_scratch_bytes() == 256 << 20
+    b = _batch(num_seqs=4, num_rows=4, max_len=1 << 24)          # 4 x 16M scores alone exceed 256 MiB
+    kidx, kv = _cache(128, seq=1 << 24), _cache(1152, seq=1 << 24)
+    st = lib.dsa_decode_noalloc(ctypes.byref(b), FAKE, None, FAKE, ctypes.byref(kidx), None, 64, 128, 2048, FAKE,
+                                ctypes.byref(kv), None, 128, 576, 512, 0.04, FAKE, FAKE, None, None)
+    assert st == _lib.DSA_ERR_WORKSPACE
+    assert "static scratch" in _err(lib)
+    st = lib.dsa_decode_noalloc(None, FAKE, None, FAKE, ctypes.byref(kidx), None, 64, 128, 2048, FAKE,
+                                ctypes.byref(kv), None, 128, 576, 512, 0.04, FAKE, FAKE, None, None)
+    assert st == _lib.DSA_ERR_NULL
