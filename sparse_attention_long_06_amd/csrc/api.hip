@@ -176,24 +176,57 @@ AttnPlan plan_attn(int T, int k, int H, int D_v) {
 // rows.  When every row sees at most k tokens (max_len <= k) the selection is
 // every prior token: no scores, no indexer, and the top-k launch only writes
 // the identity lists.
+// Decode indexer chunking: about 2048 workgroups over the batch (short enough
+// chunks that the last wave of workgroups leaves little of the device idle).
+int decode_chunk(int max_len, int num_seqs) {
+  const int64_t c = round_up(((int64_t)max_len * num_seqs + 2047) / 2048, 16);
+  return (int)(c < 256 ? 256 : (c > kIdxDecodeChunk ? kIdxDecodeChunk : c));
+}
+
+// The fused decode's chunk-candidate selection: per chunk of kCandChunk
+// tokens of a row its candidate list (key, token), count and cut key.
+struct CandPlan {
+  bool ok = false;
+  int nchunks = 0;
+  size_t off_cand = 0, off_cnt = 0, off_cut = 0, bytes = 0;
+};
+
+CandPlan plan_cand(int B, int max_len, int k) {
+  CandPlan p;
+  if (max_len <= k) return p;
+  p.nchunks = (max_len + kCandChunk - 1) / kCandChunk;
+  if (p.nchunks > kCandMaxChunks || (int64_t)B * p.nchunks >= ((int64_t)1 << 31)) return p;
+  p.ok = true;
+  size_t o = 0;
+  p.off_cand = o; o += (size_t)B * p.nchunks * kCandChunk * 8;
+  o = (size_t)round_up((int64_t)o, 256);
+  p.off_cnt = o; o += (size_t)B * p.nchunks * 4;
+  o = (size_t)round_up((int64_t)o, 256);
+  p.off_cut = o; o += (size_t)B * p.nchunks * 4;
+  p.bytes = (size_t)round_up((int64_t)o, 256);
+  return p;
+}
+
 struct FusedPlan {
   bool dense = false;
   int64_t ld = 0;
   TopkPlan tk;
+  CandPlan cd;          // decode only; shares the top-k region with tk
   AttnPlan at;
   size_t off_scores = 0, off_topk = 0, off_idx = 0, off_attn = 0, bytes = 0;
 };
 
-FusedPlan plan_fused(int T, int max_len, int k, int H, int D_v) {
+FusedPlan plan_fused(int T, int max_len, int k, int H, int D_v, bool decode) {
   FusedPlan p;
   p.dense = max_len <= k;
   p.ld = p.dense ? 0 : round_up(max_len, 4);
   if (!p.dense) p.tk = plan_topk(T, max_len, k);
+  if (!p.dense && decode) p.cd = plan_cand(T, max_len, k);
   p.at = plan_attn(T, k, H, D_v);
   size_t o = 0;
   p.off_scores = o; o += (size_t)T * p.ld * 4;
   o = (size_t)round_up((int64_t)o, 256);
-  p.off_topk = o; o += p.tk.bytes;
+  p.off_topk = o; o += p.tk.bytes > p.cd.bytes ? p.tk.bytes : p.cd.bytes;
   p.off_idx = o; o += (size_t)round_up((int64_t)T * k * 4, 256);
   p.off_attn = o; o += p.at.bytes;
   p.bytes = o;
@@ -201,7 +234,7 @@ FusedPlan plan_fused(int T, int max_len, int k, int H, int D_v) {
 }
 
 // Workspace of dsa_prefill_streaming: the compacted sampled keys, the sampled
-// score matrix [T, ceil(max_len / 16)], per-row thresholds and list headers,
+// score matrix [T, ceil(max_len / kStreamStride)], per-row thresholds and list headers,
 // the candidate lists [T, cap] and their segment records; no [T, max_len]
 // score matrix.
 struct StreamPlan {
@@ -288,10 +321,7 @@ dsa_status run_indexer(const dsa_batch* b, const uint8_t* q8, const float* q_sca
   a.H_I = H_I;
   const bool decode = b->q_start == nullptr;
   if (decode) {
-    // about 2048 workgroups over the batch: short enough chunks that the last
-    // wave of workgroups leaves little of the device idle
-    int64_t c = round_up(((int64_t)b->max_len * b->num_seqs + 2047) / 2048, 16);
-    a.chunk = (int)(c < 256 ? 256 : (c > kIdxDecodeChunk ? kIdxDecodeChunk : c));
+    a.chunk = decode_chunk(b->max_len, b->num_seqs);
     a.ntiles = 1;
   } else {
     a.chunk = kIdxPrefillChunk;
@@ -449,10 +479,10 @@ extern "C" size_t dsa_workspace_size(int entry, const dsa_batch* batch, int k, i
       return plan_attn(batch->num_rows, k, H, D_v).bytes;
     case DSA_WS_DECODE:
       if (H < 1 || D_v < 1 || batch->q_start) return (size_t)-1;
-      return plan_fused(batch->num_rows, batch->max_len, k, H, D_v).bytes;
+      return plan_fused(batch->num_rows, batch->max_len, k, H, D_v, true).bytes;
     case DSA_WS_PREFILL:
       if (H < 1 || D_v < 1 || !batch->q_start) return (size_t)-1;
-      return plan_fused(batch->num_rows, batch->max_len, k, H, D_v).bytes;
+      return plan_fused(batch->num_rows, batch->max_len, k, H, D_v, false).bytes;
     case DSA_WS_PREFILL_STREAM:
       if (H < 1 || D_v < 1 || !batch->q_start || k > kStreamMaxK) return (size_t)-1;
       return plan_stream(batch->num_seqs, batch->num_rows, batch->max_len, k, H, D_v).bytes;
@@ -520,10 +550,10 @@ extern "C" dsa_status dsa_sparse_attn(const dsa_batch* batch, const uint16_t* q,
 namespace {
 
 // The fused path over all rows of the batch, enqueued on one stream:
-// [workspace clear] -> indexer -> top-k -> attention (+ split combine), or,
-// when no row sees more than k tokens, identity selections -> attention.
-// One query per sequence (decode) gets the first top-k histogram from the
-// indexer; other batches build it in the top-k step.
+// indexer -> top-k -> attention (+ split combine), or, when no row sees more
+// than k tokens, identity selections -> attention.  One query per sequence
+// (decode) selects through per-chunk candidates (launch_topk_chunk, then
+// launch_topk_cand); other batches use the histogram top-k.
 dsa_status run_fused(const dsa_batch* batch, const uint8_t* q8, const float* q_scale, const float* w,
                      const dsa_cache* kidx, const dsa_cache* kscale, int H_I, int d_I, int k, const uint16_t* q,
                      const dsa_cache* kv, const dsa_cache* v, int H, int D, int D_v, float scale, uint16_t* out,
@@ -535,21 +565,43 @@ dsa_status run_fused(const dsa_batch* batch, const uint8_t* q8, const float* q_s
   g_stage_armed = false;
   auto mark = [&](int i) -> hipError_t { return timed ? hipEventRecord(g_stage_events[i], s) : hipSuccess; };
   const bool decode = batch->q_start == nullptr;
-  uint32_t* hist = nullptr;
-  if (!p.dense && decode && p.tk.split) {
-    hist = reinterpret_cast<uint32_t*>(tws + p.tk.off_hist);
-    LAUNCH(launch_zero(hist, (int64_t)p.tk.zero_words, s), "workspace clear");
-  }
-  LAUNCH(mark(0), "stage event");
   dsa_status st;
-  if (!p.dense) {
-    st = run_indexer(batch, q8, q_scale, w, kidx, kscale, H_I, d_I, scores, p.ld, hist, s);
+  if (!p.dense && decode && p.cd.ok) {
+    // decode: indexer scores -> per-chunk candidates -> each row's top-k
+    // among its chunks' candidates
+    LAUNCH(mark(0), "stage event");
+    st = run_indexer(batch, q8, q_scale, w, kidx, kscale, H_I, d_I, scores, p.ld, nullptr, s);
     if (st != DSA_OK) return st;
+    LAUNCH(mark(1), "stage event");
+    CandArgs c;
+    c.g = make_geo(batch);
+    c.scores = scores;
+    c.ld = p.ld;
+    c.k = k;
+    c.nchunks = p.cd.nchunks;
+    c.cand = reinterpret_cast<uint2*>(tws + p.cd.off_cand);
+    c.cand_cnt = reinterpret_cast<uint32_t*>(tws + p.cd.off_cnt);
+    c.cand_cut = reinterpret_cast<uint32_t*>(tws + p.cd.off_cut);
+    c.idx = idx;
+    LAUNCH(launch_topk_chunk(c, s), "top-k launch");
+    LAUNCH(launch_topk_cand(c, s), "top-k launch");
+    LAUNCH(mark(2), "stage event");
+  } else {
+    uint32_t* hist = nullptr;
+    if (!p.dense && decode && p.tk.split) {
+      hist = reinterpret_cast<uint32_t*>(tws + p.tk.off_hist);
+      LAUNCH(launch_zero(hist, (int64_t)p.tk.zero_words, s), "workspace clear");
+    }
+    LAUNCH(mark(0), "stage event");
+    if (!p.dense) {
+      st = run_indexer(batch, q8, q_scale, w, kidx, kscale, H_I, d_I, scores, p.ld, hist, s);
+      if (st != DSA_OK) return st;
+    }
+    LAUNCH(mark(1), "stage event");
+    st = run_topk(batch, scores, p.dense ? 4 : p.ld, k, idx, p.tk, tws, hist != nullptr, s);
+    if (st != DSA_OK) return st;
+    LAUNCH(mark(2), "stage event");
   }
-  LAUNCH(mark(1), "stage event");
-  st = run_topk(batch, scores, p.dense ? 4 : p.ld, k, idx, p.tk, tws, hist != nullptr, s);
-  if (st != DSA_OK) return st;
-  LAUNCH(mark(2), "stage event");
   st = run_attn(batch, q, kv, v, H, D, D_v, scale, idx, k, out, lse, p.at, ws + p.off_attn, s);
   if (st != DSA_OK) return st;
   LAUNCH(mark(3), "stage event");
@@ -608,7 +660,8 @@ dsa_status run_stream(const dsa_batch* batch, const uint8_t* q8, const float* q_
   LAUNCH(mark(0), "stage event");
   if (!p.dense) {
     LAUNCH(launch_stream_gather(sa, s), "sampled-key gather launch");
-    // the prefill indexer over the compacted sampled keys (key u = token 16u)
+    // the prefill indexer over the compacted sampled keys (key u = token u << kStreamShift,
+    // every kStreamStride-th token)
     IndexerArgs ia;
     ia.g = sa.g;
     ia.g.block_table = nullptr;
@@ -682,7 +735,7 @@ extern "C" dsa_status dsa_decode(const dsa_batch* batch, const uint8_t* q8, cons
   dsa_status st = check_batch(batch);
   if (st != DSA_OK) return st;
   CHECK(batch->q_start == nullptr, DSA_ERR_SHAPE, "dsa_decode takes one query per sequence (q_start must be NULL)");
-  const FusedPlan p = plan_fused(batch->num_rows, batch->max_len, k, H, D_v);
+  const FusedPlan p = plan_fused(batch->num_rows, batch->max_len, k, H, D_v, true);
   st = check_fused(batch, q8, w, kidx, kscale, H_I, d_I, k, q, kv, v, H, D, D_v, scale, out, p, workspace, ws_bytes);
   if (st != DSA_OK) return st;
   if (batch->num_rows == 0) return ok();
@@ -699,7 +752,7 @@ extern "C" dsa_status dsa_prefill(const dsa_batch* batch, const uint8_t* q8, con
   dsa_status st = check_batch(batch);
   if (st != DSA_OK) return st;
   CHECK(batch->q_start != nullptr, DSA_ERR_SHAPE, "dsa_prefill takes query rows per sequence (q_start must be set)");
-  const FusedPlan p = plan_fused(batch->num_rows, batch->max_len, k, H, D_v);
+  const FusedPlan p = plan_fused(batch->num_rows, batch->max_len, k, H, D_v, false);
   st = check_fused(batch, q8, w, kidx, kscale, H_I, d_I, k, q, kv, v, H, D, D_v, scale, out, p, workspace, ws_bytes);
   if (st != DSA_OK) return st;
   if (batch->num_rows == 0) return ok();

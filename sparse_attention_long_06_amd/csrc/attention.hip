@@ -328,12 +328,371 @@ __global__ void __launch_bounds__(512) attn_kernel(AttnArgs a) {
   }
 }
 
+// ---------------------------------------------------------------- 32 heads per wave (H = 128, D = 576)
+//
+// The production shape runs on v_mfma_f32_32x32x16_bf16, whose measured issue
+// rate on this part is 1.76x that of the 16x16x32 form.  A workgroup is four
+// waves, one per SIMD, each owning 32 heads: its q fragments (32 heads x 576
+// dims, 144 VGPRs) and its output accumulators (32 heads x 512 dims in fp32,
+// 256 registers) stay in the wave's 512-entry register file for the whole
+// split, so every K or V element read from LDS feeds 32 heads (twice the
+// reuse of 16-head waves, half the LDS traffic per FLOP).
+//   * tiles of 32 selected rows, gathered by LDS DMA into a 4-slot ring
+//     (three tiles in flight while one is computed).  Before the first tile
+//     each wave stages its q block (32 heads x 576 dims, contiguous in HBM)
+//     through slot w the same way, with 1 KB coalesced DMA instructions, and
+//     reads its fragments from there: loading them straight into registers
+//     touches 32 rows per instruction and took several microseconds;
+//   * S^T = K q^T: A = 32 rows x 16 dims of K (one ds_read_b128 per lane), B =
+//     q (registers).  Lane l ends with head l%32 and rows 8(i/4)+4(l/32)+i%4
+//     in accumulator i, so a head's softmax is 16 in-lane values and one
+//     exchange with lane l^32;
+//   * O^T += V^T P^T: A = V^T read transposed from the row-major tile with
+//     ds_read_b64_tr_b16 (a 16-lane group reads 4 rows x 16 dims and lane i
+//     receives the 4 rows of dim i; two reads give a lane the 8 rows of its
+//     K slots), B = P^T straight from the S^T accumulators (K slot j of
+//     k-step u is row 16u + 8(j/4) + 4(l/32) + j%4, the same for both
+//     operands).  Lane l then holds dims 8(i/4) + 4(l/32) + i%4 of every
+//     32-dim tile of head l%32 only: a head's rescale and final 1/l are the
+//     lane's own factors, with no exchange;
+//   * 16-byte chunk c of row r sits at chunk (c & ~7) | ((c & 7) ^ f(r)),
+//     f(r) = ((r>>1 & 1) << 2) | (r>>2 & 3): the 16 rows of a K read and the
+//     4 rows x 4 chunks of a half-wave's V read land in distinct bank groups.
+constexpr int kWideRows = 32;       // selected rows per tile
+constexpr int kWideSlots = 4;       // tiles in the LDS ring (three in flight while one is computed)
+constexpr int kWideWaves = 4;       // 32 heads each
+
+typedef float v16f __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ int wswz(int r) {
+  const int x = (r >> 1) & 7;
+  return ((x & 1) << 2) | (x >> 1);
+}
+
+__device__ __forceinline__ v16f mfma32(v8bf a, v8bf b, v16f c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Sum (or max) of a value over lanes l and l^32.
+__device__ __forceinline__ float xhalf_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float xhalf_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+constexpr int kCombineGroup = 8;      // split partials whose loads a combine thread issues together
+
+__global__ void __launch_bounds__(64 * kWideWaves) __attribute__((amdgpu_waves_per_eu(1, 1)))
+attn_wide_kernel(AttnArgs a) {
+  constexpr int D = 576, DV = 512, CH = D / 8;
+  constexpr int TILE = kWideRows * CH * 16;      // 36864 bytes
+  constexpr int KK = D / 16;                     // k-steps of S
+  constexpr int NT = DV / 32;                    // 32-dim output tiles
+  constexpr int NI = kWideRows * CH / 64;        // DMA instructions per tile (36)
+  constexpr int NIW = NI / kWideWaves;           // per wave (9)
+  constexpr int SPT = kAttnMaxSplit / (64 * kWideWaves);   // slots per thread at most (8)
+  static_assert(NI % kWideWaves == 0, "tile split");
+  __shared__ __attribute__((aligned(16))) char tiles[kWideSlots][TILE];
+  __shared__ uint32_t rowid[kAttnMaxSplit];
+  __shared__ uint32_t vmask[kAttnMaxSplit / kWideRows];
+
+  const int wg = xcd_major(blockIdx.x, gridDim.x);
+  const int split = wg % a.nsplit;
+  const int t = wg / a.nsplit;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int n32 = lane & 31, g = lane >> 5;
+  const int h0 = wave * 32;
+
+  const uint32_t ring = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)&tiles[0][0];
+  // DMA of 32 rows into ring slot `slot`: row rid(r) of `base` (rows
+  // row_stride bytes apart), 16-byte chunk c of row r to chunk
+  // (c & ~7) | ((c & 7) ^ f(r)); instruction ins fills LDS bytes
+  // [1024 ins, 1024 ins + 1024) of the slot.  This call issues instructions
+  // ins0, ins0 + 4, ... (NIW of them).  The per-lane offsets are recomputed
+  // each time (an opaque copy of the lane id keeps them from being hoisted
+  // into long-lived VGPRs); the row ids are all fetched before the first DMA
+  // is issued, so their latencies overlap.
+  auto dma_rows = [&](int slot, const char* base, int64_t row_stride, auto rid, int ins0) {
+    const uint32_t lds0 = ring + (uint32_t)(slot * TILE);
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    uint32_t row[NIW];
+    int chk[NIW];
+#pragma unroll
+    for (int m = 0; m < NIW; ++m) {
+      const int p = (ins0 + kWideWaves * m) * 64 + ln;
+      const int r = p / CH, pc = p % CH;
+      chk[m] = (pc & ~7) | ((pc & 7) ^ wswz(r));
+      row[m] = rid(r);
+    }
+#pragma unroll
+    for (int m = 0; m < NIW; ++m) {
+      const int ins = ins0 + kWideWaves * m;
+      const char* src = base + (int64_t)row[m] * row_stride + chk[m] * 16;
+      const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds0 + ins * 1024);
+      asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" :: "s"(m0), "v"(src) : "memory");
+    }
+  };
+  // tile `tile` of the selected rows: the four waves share its DMA instructions
+  auto gather = [&](int tile) {
+    const uint32_t* rid = rowid + tile * kWideRows;
+    dma_rows(tile % kWideSlots, a.kv.data, a.kv.row_stride, [&](int r) { return rid[r]; }, wave);
+  };
+
+  // Prologue.  The q block of this wave (heads h0..h0+31: 36,864 contiguous
+  // bytes) goes to slot `wave` first (all 36 of its DMA instructions are
+  // this wave's); then the selected token ids and their row ids, whose wait
+  // also covers the q DMA (issued earlier, completing in order).
+  {
+    const char* qblock = reinterpret_cast<const char*>(a.q + ((int64_t)t * a.H + h0) * D);
+#pragma unroll
+    for (int part = 0; part < kWideWaves; ++part)
+      dma_rows(wave, qblock, (int64_t)D * 2, [](int r) { return (uint32_t)r; }, part);
+  }
+  int b, pos;
+  row_seq_pos(a.g, t, b, pos);
+  const int slot_beg = split * a.per_split;
+  const int nslots = min(a.k, slot_beg + a.per_split) - slot_beg;
+  const int ntiles = (nslots + kWideRows - 1) / kWideRows;
+  const int32_t* sel = a.idx + (int64_t)t * a.k + slot_beg;
+  // token rows of the split's slots (invalid slots borrow token 0 of the
+  // sequence: finite values, zero weight) and one validity bit per slot
+  const uint32_t fallback = (uint32_t)token_row(a.g, a.kv, b, 0);
+#pragma unroll
+  for (int m = 0; m < SPT; ++m) {
+    const int i = threadIdx.x + m * 64 * kWideWaves;
+    if (i < ntiles * kWideRows) {           // whole waves: ntiles * 32 is a multiple of 32
+      int s = i < nslots ? sel[i] : -1;
+      if (s > pos) s = -1;
+      rowid[i] = s >= 0 ? (uint32_t)token_row(a.g, a.kv, b, s) : fallback;
+      const uint64_t bal = __ballot(s >= 0);
+      if ((i & 31) == 0) vmask[i >> 5] = (uint32_t)(bal >> (lane & 32));
+    }
+  }
+  // q fragments (B operand of S^T): head h0 + n32, dims 16kk + 8g .. +7, from
+  // this wave's own staging slot (its DMA is complete after vmcnt(0))
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  v8bf qf[KK];
+  {
+    const char* qs = &tiles[wave][0];
+    const int y = wswz(n32);
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk)
+      qf[kk] = *reinterpret_cast<const v8bf*>(qs + n32 * CH * 16 + (kk >> 2) * 128 + 16 * ((2 * (kk & 3) + g) ^ y));
+  }
+  __syncthreads();        // row ids published; every wave holds its q (the slots are free again)
+
+  // per-lane LDS operand offsets within a tile
+  int kb[4];
+  {
+    const int y = wswz(n32);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) kb[q] = n32 * CH * 16 + 16 * ((2 * q + g) ^ y);
+  }
+  int vb[2][2];
+  {
+    const int G = lane >> 4, i = lane & 15;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int row = 8 * h + 4 * (G >> 1) + (i >> 2);
+      const int y = wswz(row);
+#pragma unroll
+      for (int np = 0; np < 2; ++np)
+        vb[h][np] = row * CH * 16 + 16 * ((4 * np + 2 * (G & 1) + ((i & 3) >> 1)) ^ y) + 8 * (i & 1);
+    }
+  }
+
+  v16f o[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) o[nt][i] = 0.0f;
+  float m_run = -INFINITY, l_run = 0.0f;   // head n32: running max (log2 units) and this lane's partial sum
+
+  // One tile: wait for its DMA, S^T = K q^T, online softmax, O^T += V^T P^T.
+  auto step = [&](int j) {
+    // wait for tile j: the tiles after it (up to two) may stay in flight
+    if (j + 2 < ntiles) asm volatile("s_waitcnt vmcnt(%0)" :: "n"(2 * NIW) : "memory");
+    else if (j + 1 < ntiles) asm volatile("s_waitcnt vmcnt(%0)" :: "n"(NIW) : "memory");
+    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();        // tile j is in LDS; every wave is done with tile j-1
+    if (j + kWideSlots - 1 < ntiles) gather(j + kWideSlots - 1);
+    const char* kt = &tiles[j % kWideSlots][0];
+
+    // ---- S^T = K q^T over 36 k-steps, two accumulator chains in VGPRs
+    // (even and odd k-steps).  Written as inline asm so the accumulators stay
+    // in VGPRs and the output accumulators keep all 256 AGPRs.  Each chain
+    // starts from a zero SrcC and accumulates in place (SrcC = VDST, same
+    // shape); the last pair is followed by enough wait states (21) for VALU
+    // reads of an XDL result, which the compiler does not insert after inline
+    // asm.  With one wave per SIMD only the wave's own prefetch hides the LDS
+    // latency: K fragments are read four steps ahead through a 6-entry ring.
+    constexpr int KD = 4, KR = 6;
+    v16f sa, sb;
+    v8bf kr[KR];
+    auto kread = [&](int kk) -> v8bf { return *reinterpret_cast<const v8bf*>(kt + kb[kk & 3] + (kk >> 2) * 128); };
+#pragma unroll
+    for (int kk = 0; kk < KD; ++kk) kr[kk] = kread(kk);
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      if (kk + KD < KK) kr[(kk + KD) % KR] = kread(kk + KD);
+      const v8bf k0 = kr[kk % KR];
+      if (kk < 2) {
+        if (kk == 0) asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(sa) : "v"(k0), "v"(qf[kk]));
+        else asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(sb) : "v"(k0), "v"(qf[kk]));
+      } else if (kk + 1 < KK) {
+        if (kk & 1) asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(sb) : "v"(k0), "v"(qf[kk]));
+        else asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(sa) : "v"(k0), "v"(qf[kk]));
+      } else {
+        asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0\n\ts_nop 7\n\ts_nop 7\n\ts_nop 4"
+                     : "+v"(sb) : "v"(k0), "v"(qf[kk]));
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+
+    // the first V fragments of the P V product are requested before the
+    // softmax; P V runs all dim tiles of k-step u = 0 (rows 0-15), then u = 1
+    auto vread = [&](int st) -> v8bf {
+      const int nt = st & (NT - 1), u = st / NT;
+      const char* p0 = kt + u * 16 * CH * 16 + (nt >> 1) * 128;
+      const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(p0 + vb[0][nt & 1]));
+      const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(p0 + vb[1][nt & 1]));
+      return __builtin_bit_cast(v8bf, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    };
+    constexpr int VD = 4, VR = 6;
+    v8bf vr[VR];
+#pragma unroll
+    for (int st = 0; st < VD; ++st) vr[st] = vread(st);
+
+    // ---- online softmax in log2 units (lazily moved reference max, P < 2^8)
+    const uint32_t vm = vmask[j] >> (4 * g);      // bit 8(i/4) + i%4: row of accumulator i
+    float x[16];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      x[i] = ((vm >> (8 * (i >> 2) + (i & 3))) & 1u) ? (sa[i] + sb[i]) * a.scale_log2 : -INFINITY;
+      mx = fmaxf(mx, x[i]);
+    }
+    mx = xhalf_max(mx);
+    const float m_old = m_run;
+    const bool move = mx > m_old + 8.0f;
+    const float m_ref = move ? mx : m_old;
+    const float m_use = (m_ref == -INFINITY) ? 0.0f : m_ref;
+    const float alpha = (move && m_old != -INFINITY) ? __builtin_amdgcn_exp2f(m_old - m_ref) : 1.0f;
+    m_run = m_ref;
+    // P of k-step 0 (accumulators 0-7) now; that of k-step 1 is computed one
+    // value per step inside the first half of the P V loop, where its VALU
+    // work overlaps the matrix core
+    v8bf pa[2];
+    float psum = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float p = __builtin_amdgcn_exp2f(x[i] - m_use);
+      psum += p;
+      pa[0][i] = (__bf16)p;
+    }
+    // ---- rescale O^T where the head's reference moved (lane l holds head l%32
+    // only, so the factor is the lane's own).  In place in the accumulation
+    // registers, by inline asm so the accumulators never leave them; wait
+    // states before (XDL result read by VALU) and after (VALU write read as
+    // SrcC) are explicit, the compiler does not see inside the asm.
+    if (__any(alpha != 1.0f)) {
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        float tmp;
+        asm volatile(
+            "s_nop 7\n\ts_nop 7\n\ts_nop 4\n\t"
+            "v_accvgpr_read_b32 %16, %0\n\tv_mul_f32 %16, %16, %17\n\tv_accvgpr_write_b32 %0, %16\n\t"
+            "v_accvgpr_read_b32 %16, %1\n\tv_mul_f32 %16, %16, %17\n\tv_accvgpr_write_b32 %1, %16\n\t"
+            "v_accvgpr_read_b32 %16, %2\n\tv_mul_f32 %16, %16, %17\n\tv_accvgpr_write_b32 %2, %16\n\t"
+            "v_accvgpr_read_b32 %16, %3\n\tv_mul_f32 %16, %16, %17\n\tv_accvgpr_write_b32 %3, %16\n\t"
+            "v_accvgpr_read_b32 %16, %4\n\tv_mul_f32 %16, %16, %17\n\tv_accvgpr_write_b32 %4, %16\n\t"
+            "v_accvgpr_read_b32 %16, %5\n\tv_mul_f32 %16, %16, %17\n\tv_accvgpr_write_b32 %5, %16\n\t"
+            "v_accvgpr_read_b32 %16, %6\n\tv_mul_f32 %16, %16, %17\n\tv_accvgpr_write_b32 %6, %16\n\t"
+            "v_accvgpr_read_b32 %16, %7\n\tv_mul_f32 %16, %16, %17\n\tv_accvgpr_write_b32 %7, %16\n\t"
+            "v_accvgpr_read_b32 %16, %8\n\tv_mul_f32 %16, %16, %17\n\tv_accvgpr_write_b32 %8, %16\n\t"
+            "v_accvgpr_read_b32 %16, %9\n\tv_mul_f32 %16, %16, %17\n\tv_accvgpr_write_b32 %9, %16\n\t"
+            "v_accvgpr_read_b32 %16, %10\n\tv_mul_f32 %16, %16, %17\n\tv_accvgpr_write_b32 %10, %16\n\t"
+            "v_accvgpr_read_b32 %16, %11\n\tv_mul_f32 %16, %16, %17\n\tv_accvgpr_write_b32 %11, %16\n\t"
+            "v_accvgpr_read_b32 %16, %12\n\tv_mul_f32 %16, %16, %17\n\tv_accvgpr_write_b32 %12, %16\n\t"
+            "v_accvgpr_read_b32 %16, %13\n\tv_mul_f32 %16, %16, %17\n\tv_accvgpr_write_b32 %13, %16\n\t"
+            "v_accvgpr_read_b32 %16, %14\n\tv_mul_f32 %16, %16, %17\n\tv_accvgpr_write_b32 %14, %16\n\t"
+            "v_accvgpr_read_b32 %16, %15\n\tv_mul_f32 %16, %16, %17\n\tv_accvgpr_write_b32 %15, %16\n\t"
+            "s_nop 2"
+            : "+a"(o[nt][0]), "+a"(o[nt][1]), "+a"(o[nt][2]), "+a"(o[nt][3]), "+a"(o[nt][4]), "+a"(o[nt][5]),
+              "+a"(o[nt][6]), "+a"(o[nt][7]), "+a"(o[nt][8]), "+a"(o[nt][9]), "+a"(o[nt][10]), "+a"(o[nt][11]),
+              "+a"(o[nt][12]), "+a"(o[nt][13]), "+a"(o[nt][14]), "+a"(o[nt][15]), "=&v"(tmp)
+            : "v"(alpha));
+      }
+    }
+
+    // ---- O^T += V^T P^T, V read transposed from the same tile; steps st =
+    // 16u + nt, V fragments four steps ahead through a 6-entry ring
+#pragma unroll
+    for (int st = 0; st < 2 * NT; ++st) {
+      if (st + VD < 2 * NT) vr[(st + VD) % VR] = vread(st + VD);
+      if (st < 8) {
+        const float p = __builtin_amdgcn_exp2f(x[8 + st] - m_use);
+        psum += p;
+        pa[1][st] = (__bf16)p;
+      }
+      if (st == 8) l_run = l_run * alpha + psum;
+      o[st & (NT - 1)] = mfma32(vr[st % VR], pa[st / NT], o[st & (NT - 1)]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+#pragma unroll
+  for (int j0 = 0; j0 < kWideSlots - 1; ++j0)
+    if (j0 < ntiles) gather(j0);
+  for (int j = 0; j < ntiles; ++j) step(j);
+
+  // ---- finish: denominator of the lane's head, normalise, write.  Lane l
+  // holds dims 32nt + 8q + 4g + i (i < 4) of head h0 + l%32; one permlane32
+  // swap per pair of q gives each lane 8 consecutive dims (16 bytes).
+  const float l_tot = xhalf_sum(l_run);
+  const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+  const float lse_h = l_tot > 0.0f ? (m_run + __log2f(l_tot)) * 0.69314718055994531f : -INFINITY;
+  uint16_t* obase;
+  float* lbase;
+  if (a.nsplit == 1) {
+    obase = a.out + (int64_t)t * a.H * DV;
+    lbase = a.lse ? a.lse + (int64_t)t * a.H : nullptr;
+  } else {
+    const int64_t base = (int64_t)t * a.nsplit + split;
+    obase = a.part_o + base * a.H * DV;
+    lbase = a.part_lse + base * a.H;
+  }
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+#pragma unroll
+    for (int pp = 0; pp < 2; ++pp) {
+      // X: dims of q = 2pp (lane's 4 at 4g), Y: q = 2pp + 1
+      const int qa = 2 * pp, qb = 2 * pp + 1;
+      uint32_t x0 = (uint32_t)bf16_bits(o[nt][4 * qa] * inv) | ((uint32_t)bf16_bits(o[nt][4 * qa + 1] * inv) << 16);
+      uint32_t x1 = (uint32_t)bf16_bits(o[nt][4 * qa + 2] * inv) | ((uint32_t)bf16_bits(o[nt][4 * qa + 3] * inv) << 16);
+      uint32_t y0 = (uint32_t)bf16_bits(o[nt][4 * qb] * inv) | ((uint32_t)bf16_bits(o[nt][4 * qb + 1] * inv) << 16);
+      uint32_t y1 = (uint32_t)bf16_bits(o[nt][4 * qb + 2] * inv) | ((uint32_t)bf16_bits(o[nt][4 * qb + 3] * inv) << 16);
+      // lanes 32-63 of X <-> lanes 0-31 of Y: the low half ends with q = 2pp
+      // (its own dims 0-3 in X, the partner's 4-7 in Y), the high half with q = 2pp+1
+      const auto s0 = __builtin_amdgcn_permlane32_swap(x0, y0, false, false);
+      const auto s1 = __builtin_amdgcn_permlane32_swap(x1, y1, false, false);
+      const v4i v = v4i{(int)s0[0], (int)s1[0], (int)s0[1], (int)s1[1]};
+      // low half: dims 32nt + 16pp + 0..7 of head n32; high half: 32nt + 16pp + 8..15
+      *reinterpret_cast<v4i*>(obase + (int64_t)(h0 + n32) * DV + nt * 32 + 16 * pp + 8 * g) = v;
+    }
+  }
+  if (lbase && g == 0) lbase[h0 + n32] = lse_h;
+}
+
 // Merge split partials: lse = log sum_i exp(lse_i); out = sum_i exp(lse_i - lse) O_i.
 // One thread per 8 consecutive value dims of one head.  The partials are read
 // in groups of kCombineGroup splits whose loads are all issued before any is
 // used; the weights are taken relative to the largest split lse and the sum
 // is normalised once at the end.
-constexpr int kCombineGroup = 8;
 
 __global__ void __launch_bounds__(256) attn_combine_kernel(CombineArgs a) {
   const int per_head = a.D_v / 8;
@@ -396,7 +755,9 @@ __global__ void __launch_bounds__(256) attn_combine_kernel(CombineArgs a) {
 hipError_t launch_attn(const AttnArgs& a, int D, int D_v, hipStream_t stream) {
   const dim3 grid((unsigned)((int64_t)a.g.num_rows * a.nsplit));
   const bool sepv = a.v.data != nullptr;
-  if (D == 576 && D_v == 512 && !sepv) {
+  if (attn_uses_wide(a.H, D, D_v, sepv, a.per_split)) {
+    hipLaunchKernelGGL(attn_wide_kernel, grid, dim3(64 * kWideWaves), 0, stream, a);
+  } else if (D == 576 && D_v == 512 && !sepv) {
     const dim3 block(64 * ((a.H + 15) / 16));          // 16 heads per wave
     hipLaunchKernelGGL((attn_kernel<576, 512, false, 1>), grid, block, 0, stream, a);
   } else if (D == 64 && D_v == 64) {
@@ -413,6 +774,10 @@ hipError_t launch_combine(const CombineArgs& a, hipStream_t stream) {
   const int64_t items = (int64_t)a.T * a.H * (a.D_v / 8);
   hipLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)((items + 255) / 256)), dim3(256), 0, stream, a);
   return hipGetLastError();
+}
+
+bool attn_uses_wide(int H, int D, int D_v, bool sepv, int per_split) {
+  return D == 576 && D_v == 512 && !sepv && H == 32 * kWideWaves && per_split <= kAttnMaxSplit;
 }
 
 }  // namespace dsa

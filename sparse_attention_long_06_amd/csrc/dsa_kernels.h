@@ -114,6 +114,39 @@ constexpr int kTopkMaxSlices = 64;
 constexpr int kTopkSplitMaxRows = 512;
 
 hipError_t launch_zero(uint32_t* p, int64_t n, hipStream_t stream);
+// The fused decode's selection through chunk candidates: per chunk of
+// kCandChunk tokens of a row, the tokens whose keys reach the boundary of the
+// chunk's C-th largest key (C = cand_per_chunk), then the row's top-k among
+// them (exact: a row whose candidates may miss part of its top-k is selected
+// again from its scores).
+constexpr int kCandChunk = 8192;
+// Chunks per row above which the fused decode uses the histogram path instead.
+constexpr int kCandMaxChunks = 1024;
+
+// Candidates a chunk keeps at least: 1.25 times the chunk's expected share of
+// the row's top-k plus 64 (a chunk holding more of the top-k than that is
+// more than 12 standard deviations out on exchangeable scores; the selection
+// then falls back to the row's full scores), or the whole chunk.
+__host__ __device__ inline int cand_per_chunk(int k, int chunk, int n, int nk) {
+  const long long c = (5ll * k * chunk + 4ll * n - 1) / (4ll * n) + 64;
+  return c < nk ? (int)c : nk;
+}
+
+struct CandArgs {
+  Geo g;
+  const float* scores;   // [T, ld]
+  int64_t ld;
+  int k;
+  int nchunks;           // chunk slots per row: ceil(max_len / kCandChunk)
+  uint2* cand;           // [T, nchunks, kCandChunk] (key, token), token order
+  uint32_t* cand_cnt;    // [T, nchunks] candidates kept
+  uint32_t* cand_cut;    // [T, nchunks] largest key the chunk may have dropped, 0 when none
+  int32_t* idx;          // [T, k]
+};
+// One workgroup per (row, chunk): the chunk's candidates.
+hipError_t launch_topk_chunk(const CandArgs& a, hipStream_t stream);
+// One workgroup per row: the row's top-k from its chunks' candidates.
+hipError_t launch_topk_cand(const CandArgs& a, hipStream_t stream);
 hipError_t launch_topk_hist(const TopkArgs& a, hipStream_t stream);
 hipError_t launch_topk_split(const TopkArgs& a, hipStream_t stream);
 hipError_t launch_topk_row(const TopkArgs& a, hipStream_t stream);
@@ -146,6 +179,9 @@ struct CombineArgs {
   float* lse;
   int T, H, D_v, nsplit;
 };
+
+// Whether launch_attn runs the 32-head-per-wave kernel for these shapes.
+bool attn_uses_wide(int H, int D, int D_v, bool sepv, int per_split);
 
 hipError_t launch_attn(const AttnArgs& a, int D, int D_v, hipStream_t stream);
 hipError_t launch_combine(const CombineArgs& a, hipStream_t stream);

@@ -92,20 +92,22 @@ struct SegSrc {  // per-slice (key, index) lists in global memory, concatenated 
 // ---- block-level building blocks (every thread of the block calls them)
 
 // Chunks of NT*4 elements whose loads are issued together before any of
-// them is consumed: global sources are latency-bound otherwise.
+// them is consumed: global sources are latency-bound otherwise.  The
+// helpers below take the count as a template argument U (default kUnr);
+// their LDS scratch `tmp` holds U * NT/64 words.
 constexpr int kUnr = 8;
 
-// kUnr chunks of 4 elements per thread starting at `base`; whole chunks go
+// U chunks of 4 elements per thread starting at `base`; whole chunks go
 // through load4_full (issued back to back), a ragged batch through load4.
-template <int NT, class Src>
-__device__ __forceinline__ void load_batch(const Src& src, int base, uint32_t (&key)[kUnr][4], int (&id)[kUnr][4],
-                                           bool (&ok)[kUnr][4]) {
-  if (base + NT * 4 * kUnr <= src.size()) {       // uniform
+template <int NT, int U = kUnr, class Src>
+__device__ __forceinline__ void load_batch(const Src& src, int base, uint32_t (&key)[U][4], int (&id)[U][4],
+                                           bool (&ok)[U][4]) {
+  if (base + NT * 4 * U <= src.size()) {       // uniform
 #pragma unroll
-    for (int u = 0; u < kUnr; ++u) src.load4_full(base + (u * NT + threadIdx.x) * 4, key[u], id[u], ok[u]);
+    for (int u = 0; u < U; ++u) src.load4_full(base + (u * NT + threadIdx.x) * 4, key[u], id[u], ok[u]);
   } else {
 #pragma unroll
-    for (int u = 0; u < kUnr; ++u) src.load4(base + (u * NT + threadIdx.x) * 4, key[u], id[u], ok[u]);
+    for (int u = 0; u < U; ++u) src.load4(base + (u * NT + threadIdx.x) * 4, key[u], id[u], ok[u]);
   }
 }
 
@@ -123,20 +125,20 @@ __device__ __forceinline__ void load_hist(const uint32_t* gh, uint32_t* hist) {
 }
 
 // Histogram of bits [shift, shift+bits) of the keys whose top `pbits` bits equal P.
-template <int NT, class Src>
+template <int NT, int U = kUnr, class Src>
 __device__ __forceinline__ void hist_pass(const Src& src, uint32_t* hist, uint32_t P, int pbits, int shift, int bits) {
   const int nb = 1 << bits;
   for (int i = threadIdx.x; i < nb; i += NT) hist[i] = 0u;
   lds_barrier();
   const uint32_t mask = (uint32_t)nb - 1u;
   const int n = src.size();
-  for (int base = 0; base < n; base += NT * 4 * kUnr) {
-    uint32_t key[kUnr][4];
-    int id[kUnr][4];
-    bool ok[kUnr][4];
-    load_batch<NT>(src, base, key, id, ok);
+  for (int base = 0; base < n; base += NT * 4 * U) {
+    uint32_t key[U][4];
+    int id[U][4];
+    bool ok[U][4];
+    load_batch<NT, U>(src, base, key, id, ok);
 #pragma unroll
-    for (int u = 0; u < kUnr; ++u)
+    for (int u = 0; u < U; ++u)
 #pragma unroll
       for (int j = 0; j < 4; ++j)
         if (ok[u][j] && (pbits == 0 || (key[u][j] >> (32 - pbits)) == P))
@@ -182,27 +184,27 @@ __device__ __forceinline__ BinSel select_bin(const uint32_t* hist, int nb, uint3
 // top-`pbits` key prefix is greater than P plus the first `need_eq` whose
 // prefix equals P; emit(slot, key, index) gets consecutive slots.
 //
-// compact_batch does one batch already in registers (kUnr chunks of 4
+// compact_batch does one batch already in registers (U chunks of 4
 // elements per thread, chunk u covering elements (u*NT + thread)*4 + j).  The
-// kUnr packed (greater, equal) chunk counts are scanned together, one barrier
+// U packed (greater, equal) chunk counts are scanned together, one barrier
 // pair per batch, and each thread then walks only its set bits, so the cost
 // follows the few elements kept.  gt_base / eq_base (uniform) count the
 // elements of earlier batches and are advanced past this one.  tmp holds
-// kUnr * NT/64 words.
-template <int NT, class Emit>
-__device__ __forceinline__ void compact_batch(const uint32_t (&key)[kUnr][4], const int (&id)[kUnr][4],
-                                              const bool (&ok)[kUnr][4], uint32_t P, int shift, uint32_t need_eq,
+// U * NT/64 words.
+template <int NT, int U = kUnr, class Emit>
+__device__ __forceinline__ void compact_batch(const uint32_t (&key)[U][4], const int (&id)[U][4],
+                                              const bool (&ok)[U][4], uint32_t P, int shift, uint32_t need_eq,
                                               uint32_t* tmp, uint32_t& gt_base, uint32_t& eq_base, Emit& emit) {
   constexpr int NW = NT / 64;
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-  uint32_t mg[kUnr], me[kUnr], inc[kUnr], own[kUnr];
+  uint32_t mg[U], me[U], inc[U], own[U];
 #pragma unroll
-  for (int u = 0; u < kUnr; ++u) {
+  for (int u = 0; u < U; ++u) {
     mg[u] = 0u;
     me[u] = 0u;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {        // branch-free: selects, no exec-mask juggling
-      const uint32_t pre = key[u][j] >> shift;
+      const uint32_t pre = shift < 32 ? key[u][j] >> shift : 0u;   // shift 32: no prefix yet
       const uint32_t v = ok[u][j] ? 1u : 0u;
       mg[u] |= (v & (pre > P ? 1u : 0u)) << j;
       me[u] |= (v & (pre == P ? 1u : 0u)) << j;
@@ -212,10 +214,10 @@ __device__ __forceinline__ void compact_batch(const uint32_t (&key)[kUnr][4], co
     if (lane == 63) tmp[u * NW + wid] = inc[u];
   }
   lds_barrier();
-  uint32_t gt0[kUnr], eq0[kUnr];
+  uint32_t gt0[U], eq0[U];
   uint32_t rg = gt_base, re = eq_base;
 #pragma unroll
-  for (int u = 0; u < kUnr; ++u) {
+  for (int u = 0; u < U; ++u) {
     uint32_t before = 0, tot = 0;
 #pragma unroll
     for (int w = 0; w < NW; ++w) {
@@ -233,7 +235,7 @@ __device__ __forceinline__ void compact_batch(const uint32_t (&key)[kUnr][4], co
   gt_base = rg;
   eq_base = re;
 #pragma unroll
-  for (int u = 0; u < kUnr; ++u) {
+  for (int u = 0; u < U; ++u) {
     uint32_t mm = mg[u] | me[u], gt = gt0[u], eq = eq0[u];
     while (mm) {
       const int j = __builtin_ctz(mm);
@@ -253,39 +255,40 @@ __device__ __forceinline__ void compact_batch(const uint32_t (&key)[kUnr][4], co
 
 // Whole-source ordered compaction; stops after the batch in which `target`
 // elements are out.  Returns the number emitted (uniform).
-template <int NT, class Src, class Emit>
+template <int NT, int U = kUnr, class Src, class Emit>
 __device__ __forceinline__ uint32_t compact(const Src& src, uint32_t P, int pbits, uint32_t need_eq,
                                             uint32_t target, uint32_t* tmp, Emit emit) {
   const int shift = 32 - pbits;
   uint32_t gt_base = 0, eq_base = 0;
   const int n = src.size();
-  for (int base = 0; base < n; base += NT * 4 * kUnr) {
-    uint32_t key[kUnr][4];
-    int id[kUnr][4];
-    bool ok[kUnr][4];
-    load_batch<NT>(src, base, key, id, ok);
-    compact_batch<NT>(key, id, ok, P, shift, need_eq, tmp, gt_base, eq_base, emit);
+  for (int base = 0; base < n; base += NT * 4 * U) {
+    uint32_t key[U][4];
+    int id[U][4];
+    bool ok[U][4];
+    load_batch<NT, U>(src, base, key, id, ok);
+    compact_batch<NT, U>(key, id, ok, P, shift, need_eq, tmp, gt_base, eq_base, emit);
     if (gt_base + min(eq_base, need_eq) >= target) break;
   }
   return gt_base + min(eq_base, need_eq);
 }
 
 // Refine (P, pbits) until the boundary bin is needed whole or the key is
-// exhausted, then emit the selection in source order.
-template <int NT, class Src, class Emit>
+// exhausted, then emit the selection in source order.  pbits may start
+// anywhere in [0, 32] (0: no prefix yet); each pass takes up to 11 more bits.
+template <int NT, int U = kUnr, class Src, class Emit>
 __device__ __forceinline__ void refine_and_emit(const Src& src, uint32_t P, int pbits, uint32_t need, uint32_t cnt,
                                 uint32_t* hist, uint32_t* tmp, BinSel* res, uint32_t target, Emit emit) {
   while (cnt != need && pbits < 32) {
-    const int bits = (pbits + 11 <= 22) ? 11 : 32 - pbits;
+    const int bits = 32 - pbits < kBins1Bits ? 32 - pbits : kBins1Bits;
     const int shift = 32 - pbits - bits;
-    hist_pass<NT>(src, hist, P, pbits, shift, bits);
+    hist_pass<NT, U>(src, hist, P, pbits, shift, bits);
     const BinSel s = select_bin<NT>(hist, 1 << bits, need, tmp, res);
     P = (P << bits) | s.bin;
     pbits += bits;
     need -= s.above;
     cnt = s.cnt;
   }
-  compact<NT>(src, P, pbits, need, target, tmp, emit);
+  compact<NT, U>(src, P, pbits, need, target, tmp, emit);
 }
 
 __device__ __forceinline__ void write_identity(int32_t* out, int n, int k, int tid, int nt) {

@@ -260,6 +260,453 @@ __global__ void __launch_bounds__(kFinalNT) topk_finalize_kernel(TopkArgs a) {
   }
 }
 
+// ---------------------------------------------------------------- chunk-candidate mode (fused decode)
+//
+// Two launches after the indexer has written a row's scores:
+//
+//   chunk   one workgroup per (row, chunk of kCandChunk tokens) keeps the
+//           chunk's keys whose top 22 bits reach the boundary of its C-th
+//           largest key (C = cand_per_chunk), in token order, with the
+//           largest key it may have dropped (its cut).  Every workgroup of
+//           the launch is resident at once, so this costs about one read of
+//           the scores plus a few LDS passes.
+//   merge   one workgroup per row stages the chunks' lists in LDS and selects
+//           the row's top-k among them.  A dropped element can only belong to
+//           the top-k (or tie its k-th key) when its chunk's cut reaches the
+//           k-th key; then the row is selected again from its full scores, so
+//           the result is always exact.
+//
+// Keys are ranked within [lo, hi] of the staged candidates: the radix passes
+// run over key - lo from its highest possibly set bit, which spreads the
+// candidates (all from the upper tail of the row) over the histogram bins
+// instead of piling them into the few bins their top 11 bits share.
+
+// Selection steps shared by the two launches.  Elements stay in registers:
+// a thread owns PER consecutive elements, so source order is (thread, slot)
+// order and an ordered compaction needs one block scan.  The boundary bin of
+// a histogram is found by wave 0 alone while the other waves clear the
+// histogram of the next pass (two alternate), so a pass costs two barriers.
+
+// Top `pbits` bits of a key (0 when pbits is 0).
+__device__ __forceinline__ uint32_t key_prefix(uint32_t key, int pbits) {
+  return pbits == 0 ? 0u : key >> (32 - pbits);
+}
+
+// Wave-wide min / max with DPP row shifts and row broadcasts (the pattern of
+// wave_inclusive_scan; lanes with no source read the identity), then lane 63.
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t x) {
+  constexpr int kId = -1;                          // 0xFFFFFFFF
+  x = min(x, (uint32_t)__builtin_amdgcn_update_dpp(kId, (int)x, 0x111, 0xf, 0xf, false));
+  x = min(x, (uint32_t)__builtin_amdgcn_update_dpp(kId, (int)x, 0x112, 0xf, 0xf, false));
+  x = min(x, (uint32_t)__builtin_amdgcn_update_dpp(kId, (int)x, 0x114, 0xf, 0xf, false));
+  x = min(x, (uint32_t)__builtin_amdgcn_update_dpp(kId, (int)x, 0x118, 0xf, 0xf, false));
+  x = min(x, (uint32_t)__builtin_amdgcn_update_dpp(kId, (int)x, 0x142, 0xa, 0xf, false));
+  x = min(x, (uint32_t)__builtin_amdgcn_update_dpp(kId, (int)x, 0x143, 0xc, 0xf, false));
+  return (uint32_t)__builtin_amdgcn_readlane((int)x, 63);
+}
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xf, 0xf, false));
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xf, 0xf, false));
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xf, 0xf, false));
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xf, 0xf, false));
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x142, 0xa, 0xf, false));
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x143, 0xc, 0xf, false));
+  return (uint32_t)__builtin_amdgcn_readlane((int)x, 63);
+}
+
+// Wave 0 only: the bin of hist[0, nb) (nb <= kBins1, a power of two),
+// scanning from the top, where the running count reaches `need`, the count
+// above it and its own count, written to *res.  Two wave scans: lane l sums
+// the `per` bins at descending positions per*l .. per*l + per - 1 (bin
+// nb - 1 - position); then lanes 0 .. per-1 scan the bins of the lane whose
+// range holds the boundary.
+__device__ __forceinline__ void wave_select_bin(const uint32_t* hist, int nb, uint32_t need, BinSel* res) {
+  static_assert(kBins1 == 64 * 32, "at most 32 bins per lane");
+  const int lane = threadIdx.x & 63;
+  const int per = nb >= 64 ? nb >> 6 : 1;
+  uint32_t c = 0;
+  if (per == 32) {
+    const uint4* p = reinterpret_cast<const uint4*>(hist + nb - 32 * (lane + 1));
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const uint4 x = p[q];
+      c += x.x + x.y + x.z + x.w;
+    }
+  } else {
+    for (int j = 0; j < per; ++j) {
+      const int d = lane * per + j;
+      if (d < nb) c += hist[nb - 1 - d];
+    }
+  }
+  const uint32_t incl = wave_inclusive_scan(c);
+  const unsigned long long hit = __ballot(incl - c < need && need <= incl);
+  if (hit == 0ull) return;                         // need exceeds the histogram's total (callers never ask)
+  const int L = __builtin_ctzll(hit);
+  const uint32_t run0 = (uint32_t)__shfl((int)(incl - c), L);
+  const int d = L * per + lane;
+  const uint32_t v = (lane < per && d < nb) ? hist[nb - 1 - d] : 0u;
+  const uint32_t incl2 = wave_inclusive_scan(v) + run0;
+  if (lane < per && incl2 - v < need && need <= incl2) {
+    res->bin = (uint32_t)(nb - 1 - d);
+    res->above = incl2 - v;
+    res->cnt = v;
+  }
+}
+
+// Radix passes over register-held keys (PER per thread, bit j of vm set for
+// the valid ones) until the boundary prefix is exact or needed whole, or
+// pbits reaches max_pbits.  hist[0] and hist[1] must be clear on entry; P /
+// pbits / need / cnt carry the state in and out (cnt: keys sharing the
+// current prefix; need: how many of them the selection takes, <= cnt).
+template <int NT, int PER>
+__device__ __forceinline__ void reg_radix(const uint32_t (&key)[PER], uint32_t vm, uint32_t (*hist)[kBins1],
+                                          BinSel* res, uint32_t& P, int& pbits, uint32_t& need, uint32_t& cnt,
+                                          int max_pbits = 32) {
+  static_assert(PER <= 32, "32-bit validity mask");
+  const int wid = threadIdx.x >> 6;
+  int cur = 0;
+  while (cnt != need && pbits < max_pbits) {       // uniform
+    const int bits = 32 - pbits < kBins1Bits ? 32 - pbits : kBins1Bits;
+    const int shift = 32 - pbits - bits;
+    const uint32_t mask = (1u << bits) - 1u;
+    uint32_t* hc = hist[cur];
+#pragma unroll
+    for (int j = 0; j < PER; ++j)
+      if (((vm >> j) & 1u) && key_prefix(key[j], pbits) == P) atomicAdd(&hc[(key[j] >> shift) & mask], 1u);
+    lds_barrier();                                 // the histogram is complete
+    if (wid == 0) {
+      wave_select_bin(hc, 1 << bits, need, res);
+    } else {
+      uint32_t* hn = hist[cur ^ 1];
+      for (int i = threadIdx.x - 64; i < kBins1; i += NT - 64) hn[i] = 0u;
+    }
+    lds_barrier();                                 // *res is set, the next histogram clear
+    const BinSel s = *res;
+    P = (P << bits) | s.bin;
+    pbits += bits;
+    need -= s.above;
+    cnt = s.cnt;
+    cur ^= 1;
+  }
+}
+
+// ---- launch 1: per-chunk candidates
+
+constexpr int kChunkNT = 512;
+constexpr int kChunkPer = kCandChunk / kChunkNT;   // consecutive scores per thread
+static_assert(kChunkPer % 4 == 0 && kChunkPer <= 32, "float4 loads, 32-bit keep mask");
+
+__global__ void __launch_bounds__(kChunkNT) topk_chunk_kernel(CandArgs a) {
+  __shared__ __attribute__((aligned(16))) uint32_t hist[2][kBins1];
+  __shared__ uint32_t tmp[kChunkNT / 64];
+  __shared__ BinSel res;
+
+  const int t = blockIdx.x / a.nchunks;
+  const int ch = blockIdx.x - t * a.nchunks;
+  int b, pos;
+  row_seq_pos(a.g, t, b, pos);
+  const int n = pos + 1;
+  const int kbeg = ch * kCandChunk;
+  if (n <= a.k || kbeg >= n) return;          // uniform over the workgroup
+  const int nk = min(kCandChunk, n - kbeg);
+  const float* src = a.scores + (int64_t)t * a.ld + kbeg;
+  const int64_t slot0 = (int64_t)t * a.nchunks + ch;
+  uint2* out = a.cand + slot0 * kCandChunk;
+
+  // consecutive scores per thread (16-byte aligned: ld and kbeg are multiples of 4)
+  const int i0 = threadIdx.x * kChunkPer;
+  const int nv = max(0, min(kChunkPer, nk - i0));
+  uint32_t key[kChunkPer];
+  if (nv == kChunkPer) {
+    float4 v[kChunkPer / 4];
+#pragma unroll
+    for (int j = 0; j < kChunkPer / 4; ++j) v[j] = *reinterpret_cast<const float4*>(src + i0 + 4 * j);
+#pragma unroll
+    for (int j = 0; j < kChunkPer / 4; ++j) {
+      key[4 * j] = score_key(v[j].x);
+      key[4 * j + 1] = score_key(v[j].y);
+      key[4 * j + 2] = score_key(v[j].z);
+      key[4 * j + 3] = score_key(v[j].w);
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < kChunkPer; ++j) key[j] = j < nv ? score_key(src[i0 + j]) : 0u;
+  }
+
+  uint32_t vm = 0u;
+#pragma unroll
+  for (int j = 0; j < kChunkPer; ++j) vm |= (j < nv ? 1u : 0u) << j;
+
+  // keep the keys whose top `pbits` bits are >= P: two 11-bit passes leave
+  // the C largest plus the rest of their 22-bit boundary bin.  (Ranking
+  // inside a window below the chunk's largest key spreads the LDS atomics
+  // better, but the reduction that finds that key cost more than it saved.)
+  uint32_t P = 0;
+  int pbits = 0;
+  const uint32_t C = (uint32_t)cand_per_chunk(a.k, kCandChunk, n, nk);
+  if (C < (uint32_t)nk) {
+    for (int i = threadIdx.x; i < 2 * kBins1; i += kChunkNT) (&hist[0][0])[i] = 0u;
+    lds_barrier();
+    uint32_t need = C, cnt = (uint32_t)nk;
+    reg_radix<kChunkNT, kChunkPer>(key, vm, hist, &res, P, pbits, need, cnt, 2 * kBins1Bits);
+  }
+  uint32_t keep = 0u;
+#pragma unroll
+  for (int j = 0; j < kChunkPer; ++j) keep |= (((vm >> j) & 1u) && key_prefix(key[j], pbits) >= P ? 1u : 0u) << j;
+  uint32_t tot;
+  uint32_t o = block_exclusive_scan<kChunkNT>((uint32_t)__popc(keep), tmp, tot);
+#pragma unroll
+  for (int j = 0; j < kChunkPer; ++j)
+    if ((keep >> j) & 1u) out[o++] = make_uint2(key[j], (uint32_t)(kbeg + i0 + j));
+  if (threadIdx.x == 0) {
+    a.cand_cnt[slot0] = tot;
+    // dropped keys have a top-pbits prefix below P: at most (P << (32 - pbits)) - 1
+    a.cand_cut[slot0] = (pbits > 0 && P > 0u) ? (P << (32 - pbits)) - 1u : 0u;
+  }
+}
+
+hipError_t launch_topk_chunk(const CandArgs& a, hipStream_t stream) {
+  const int64_t nb = (int64_t)a.g.num_rows * a.nchunks;
+  if (nb <= 0 || nb >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(topk_chunk_kernel, dim3((unsigned)nb), dim3(kChunkNT), 0, stream, a);
+  return hipGetLastError();
+}
+
+// ---- launch 2: each row's top-k among its chunks' candidates
+
+constexpr int kCandNT = 1024;
+constexpr int kCandCap = 8192;                     // candidates held on chip; more are read in place
+constexpr int kCandPer = kCandCap / kCandNT;       // register-held candidates per thread
+constexpr int kCandLoad = 8;                       // staged entries per thread and batch
+constexpr int kCandUnr = 2;                        // load batches of the in-place and fallback passes
+constexpr int kCandOut = 2048;                     // selections staged in LDS when k fits
+
+// The candidate lists read in place (more candidates than LDS holds).
+struct CandSrc {
+  const uint2* lists;
+  const uint32_t* offs;  // LDS [nch + 1]
+  int nch;
+  int stride;
+  __device__ int size() const { return (int)offs[nch]; }
+  __device__ __forceinline__ void load4(int i, uint32_t (&k)[4], int (&d)[4], bool (&ok)[4]) const {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t pos = (uint32_t)(i + j);
+      ok[j] = pos < offs[nch];
+      k[j] = 0u;
+      d[j] = -1;
+      if (ok[j]) {
+        int lo = 0, hi = nch - 1;  // last chunk with offs[c] <= pos
+        while (lo < hi) {
+          const int mid = (lo + hi + 1) >> 1;
+          if (offs[mid] <= pos) lo = mid; else hi = mid - 1;
+        }
+        const uint2 e = lists[(int64_t)lo * stride + (pos - offs[lo])];
+        k[j] = e.x;
+        d[j] = (int)e.y;
+      }
+    }
+  }
+  __device__ __forceinline__ void load4_full(int i, uint32_t (&k)[4], int (&d)[4], bool (&ok)[4]) const { load4(i, k, d, ok); }
+};
+
+__global__ void __launch_bounds__(kCandNT) topk_cand_kernel(CandArgs a) {
+  constexpr int NW = kCandNT / 64;
+  __shared__ __attribute__((aligned(16))) uint32_t hist[2][kBins1];
+  __shared__ uint32_t tmp[kUnr * NW];
+  __shared__ uint32_t red[2 * NW];
+  __shared__ BinSel res;
+  __shared__ __attribute__((aligned(16))) uint32_t lkey[kCandCap];
+  __shared__ __attribute__((aligned(16))) int lidx[kCandCap];
+  __shared__ uint32_t offs[kCandMaxChunks + 1];
+  __shared__ int obuf[kCandOut];
+
+  const int t = blockIdx.x;
+  int b, pos;
+  row_seq_pos(a.g, t, b, pos);
+  const int n = pos + 1;
+  int32_t* out = a.idx + (int64_t)t * a.k;
+  const uint32_t k = (uint32_t)a.k;
+  if (n <= a.k) {
+    write_identity(out, n, a.k, threadIdx.x, kCandNT);
+    return;
+  }
+  const int nch = (n + kCandChunk - 1) / kCandChunk;
+  const uint32_t* cnt = a.cand_cnt + (int64_t)t * a.nchunks;
+  const uint32_t* cut = a.cand_cut + (int64_t)t * a.nchunks;
+  const uint2* lists = a.cand + (int64_t)t * a.nchunks * kCandChunk;
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+
+  // chunk offsets (one block scan of per-thread chunk counts) and the
+  // largest cut of the row, in one barrier pair
+  uint32_t m, cutmax;
+  {
+    constexpr int PERC = (kCandMaxChunks + kCandNT - 1) / kCandNT;
+    uint32_t c[PERC], sum = 0, cm = 0;
+#pragma unroll
+    for (int j = 0; j < PERC; ++j) {
+      const int ch = threadIdx.x * PERC + j;
+      c[j] = ch < nch ? cnt[ch] : 0u;
+      cm = max(cm, ch < nch ? cut[ch] : 0u);
+      sum += c[j];
+    }
+    const uint32_t x = wave_inclusive_scan(sum);
+    cm = wave_max_u32(cm);
+    if (lane == 63) tmp[wid] = x;
+    if (lane == 0) red[wid] = cm;
+    lds_barrier();
+    uint32_t before = 0, tot = 0;
+    cutmax = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const uint32_t s = tmp[w];
+      before += (w < wid) ? s : 0u;
+      tot += s;
+      cutmax = max(cutmax, red[w]);
+    }
+    uint32_t run = before + x - sum;
+#pragma unroll
+    for (int j = 0; j < PERC; ++j) {
+      const int ch = threadIdx.x * PERC + j;
+      if (ch < nch) offs[ch] = run;
+      run += c[j];
+    }
+    if (threadIdx.x == 0) offs[nch] = tot;
+    m = tot;
+  }
+  lds_barrier();                                   // offs is set; tmp / red are free again
+  const bool obuf_ok = k <= (uint32_t)kCandOut;
+  uint32_t mn = 0xFFFFFFFFu;                       // smallest key emitted (the k-th key)
+  uint32_t sub = 0u;                               // keys are ranked as key - sub
+  auto emit = [&](uint32_t slot, uint32_t key, int id) {
+    if (obuf_ok) obuf[slot] = id; else out[slot] = id;
+    mn = min(mn, key);
+  };
+  if (m <= (uint32_t)kCandCap) {
+    // stage the lists in LDS in row order: tpc threads (a power of two) per
+    // chunk, kCandLoad entries per thread and batch, every load of a batch
+    // issued before any is stored, so one batch costs one memory latency
+    int tpc = kCandNT;
+    while (tpc > 1 && tpc * nch > kCandNT) tpc >>= 1;
+    const int l = threadIdx.x & (tpc - 1);
+    uint32_t lo = 0xFFFFFFFFu, hi = 0u;
+    for (int ch = threadIdx.x / tpc; ch < nch; ch += kCandNT / tpc) {
+      const uint32_t o = offs[ch], c = offs[ch + 1] - o;
+      const uint2* src = lists + (int64_t)ch * kCandChunk;
+      for (uint32_t base = 0; base < c; base += (uint32_t)(kCandLoad * tpc)) {
+        uint2 e[kCandLoad];
+#pragma unroll
+        for (int j = 0; j < kCandLoad; ++j) {
+          const uint32_t p = base + (uint32_t)(l + j * tpc);
+          e[j] = p < c ? src[p] : make_uint2(0u, 0u);
+        }
+#pragma unroll
+        for (int j = 0; j < kCandLoad; ++j) {
+          const uint32_t p = base + (uint32_t)(l + j * tpc);
+          if (p < c) {
+            lkey[o + p] = e[j].x;
+            lidx[o + p] = (int)e[j].y;
+            lo = min(lo, e[j].x);
+            hi = max(hi, e[j].x);
+          }
+        }
+      }
+    }
+    for (int i = threadIdx.x; i < 2 * kBins1; i += kCandNT) (&hist[0][0])[i] = 0u;
+    lo = wave_min_u32(lo);
+    hi = wave_max_u32(hi);
+    // (tmp[NW..2NW): the compaction scan below writes tmp[0..NW) with no
+    // barrier in between when no radix pass runs)
+    if (lane == 0) {
+      tmp[NW + wid] = lo;
+      red[wid] = hi;
+    }
+    lds_barrier();                                 // lists staged, histograms clear, ranges in
+    lo = 0xFFFFFFFFu;
+    hi = 0u;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      lo = min(lo, tmp[NW + w]);
+      hi = max(hi, red[w]);
+    }
+    sub = lo;
+    // thread-owned consecutive candidates, as key - lo: the passes start at
+    // the highest bit that key - lo can have set
+    const int i0 = threadIdx.x * kCandPer;
+    const int nv = max(0, min(kCandPer, (int)m - i0));
+    uint32_t key[kCandPer];
+    int id[kCandPer];
+    if (nv == kCandPer) {
+#pragma unroll
+      for (int q = 0; q < kCandPer / 4; ++q) {
+        const uint4 kv = *reinterpret_cast<const uint4*>(lkey + i0 + 4 * q);
+        const int4 iv = *reinterpret_cast<const int4*>(lidx + i0 + 4 * q);
+        key[4 * q] = kv.x - sub; key[4 * q + 1] = kv.y - sub; key[4 * q + 2] = kv.z - sub; key[4 * q + 3] = kv.w - sub;
+        id[4 * q] = iv.x; id[4 * q + 1] = iv.y; id[4 * q + 2] = iv.z; id[4 * q + 3] = iv.w;
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < kCandPer; ++j) {
+        key[j] = j < nv ? lkey[i0 + j] - sub : 0u;
+        id[j] = j < nv ? lidx[i0 + j] : -1;
+      }
+    }
+    uint32_t P = 0, need = k, cb = m;
+    int pbits = hi > lo ? __clz(hi - lo) : 32;
+    const uint32_t vm = nv >= 32 ? 0xFFFFFFFFu : (1u << nv) - 1u;
+    reg_radix<kCandNT, kCandPer>(key, vm, hist, &res, P, pbits, need, cb);
+    // ordered compaction: every key above prefix P, and the first `need` at it
+    uint32_t gm = 0u, em = 0u;
+#pragma unroll
+    for (int j = 0; j < kCandPer; ++j) {
+      const uint32_t pre = key_prefix(key[j], pbits);
+      gm |= (j < nv && pre > P ? 1u : 0u) << j;
+      em |= (j < nv && pre == P ? 1u : 0u) << j;
+    }
+    uint32_t tot2;
+    const uint32_t ex = block_exclusive_scan<kCandNT>((uint32_t)__popc(gm) | ((uint32_t)__popc(em) << 16), tmp, tot2);
+    uint32_t gr = ex & 0xFFFFu, er = ex >> 16;
+#pragma unroll
+    for (int j = 0; j < kCandPer; ++j) {
+      if ((gm >> j) & 1u) {
+        emit(gr + min(er, need), key[j], id[j]);
+        ++gr;
+      } else if ((em >> j) & 1u) {
+        if (er < need) emit(gr + er, key[j], id[j]);
+        ++er;
+      }
+    }
+  } else {
+    const CandSrc src{lists, offs, nch, kCandChunk};
+    refine_and_emit<kCandNT, kCandUnr>(src, 0u, 0, k, m, hist[0], tmp, &res, k, emit);
+  }
+  mn = wave_min_u32(mn);
+  if (lane == 0) red[wid] = mn;
+  lds_barrier();                                   // obuf complete, minima in
+  uint32_t kth = 0xFFFFFFFFu;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) kth = min(kth, red[w]);
+  kth += sub;
+  // a chunk whose cut reaches the k-th key may hide elements of the top-k
+  // (or ties of it): then the row is selected again from its scores
+  if (cutmax == 0u || cutmax < kth) {
+    if (obuf_ok)
+      for (int i = threadIdx.x; i < a.k; i += kCandNT) out[i] = obuf[i];
+  } else {
+    const RowSrc row{a.scores + (int64_t)t * a.ld, n, 0};
+    hist_pass<kCandNT, kCandUnr>(row, hist[0], 0u, 0, 32 - kBins1Bits, kBins1Bits);
+    const BinSel s1 = select_bin<kCandNT>(hist[0], kBins1, k, tmp, &res);
+    refine_and_emit<kCandNT, kCandUnr>(row, s1.bin, kBins1Bits, k - s1.above, s1.cnt, hist[0], tmp, &res, k,
+                                       [&](uint32_t slot, uint32_t, int id) { out[slot] = id; });
+  }
+}
+
+hipError_t launch_topk_cand(const CandArgs& a, hipStream_t stream) {
+  hipLaunchKernelGGL(topk_cand_kernel, dim3(a.g.num_rows), dim3(kCandNT), 0, stream, a);
+  return hipGetLastError();
+}
+
 // Clears n words; 16-byte stores for the whole quads when p is 16-byte aligned.
 __global__ void zero_u32_kernel(uint32_t* p, int64_t n) {
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;

@@ -317,6 +317,54 @@ def test_fused_decode_matches_staged_bitwise(wl):
     assert torch.equal(lse_g, lse_f)
 
 
+def _decode_against_staged_and_oracle(inp, what, exact):
+    wl = inp.wl
+    batch = dsa.Batch.from_inputs(inp)
+    idx_f = torch.empty((inp.num_rows, wl.k), dtype=torch.int32, device=DEV)
+    out_f, lse_f, _ = dsa.decode(batch, inp.q8, inp.q_scale, inp.w, inp.k8, inp.k_scale, wl.k, inp.q, inp.kv,
+                                 inp.v, wl.scale, idx_out=idx_f, D_v=wl.D_v)
+    scores, idx_s, out_s, lse_s = gpu_staged(inp)
+    torch.cuda.synchronize()
+    assert torch.equal(idx_f, idx_s), f"{what}: fused selection differs from the staged top-k"
+    assert torch.equal(out_f.view(torch.int16), out_s.view(torch.int16)), f"{what}: output differs"
+    a = arrays_of(inp)
+    rows = list(range(inp.num_rows))
+    ref = oracle_rows(a, rows)
+    g_idx, g_out, g_lse = to_np(idx_f), to_np(out_f), to_np(lse_f)
+    if exact:
+        for r in rows:
+            assert np.array_equal(g_idx[r], ref["idx"][r]), f"{what} row {r}: selection not exact"
+    check_rows(a, rows, g_idx, g_out, g_lse, ref, wl.k, what, min_same=1.0 if exact else 0.9)
+
+
+def test_fused_decode_chunk_holding_the_top_k():
+    """Integer indexer inputs where 3000 consecutive tokens of every sequence
+    score far above the rest (and tie among themselves): the decode chunks
+    they fill hold more of the top-k than their candidate lists keep, so the
+    fused selection must notice the cut and select those rows again from
+    their full scores; the result is the exact top-k (lowest tokens among
+    the ties)."""
+    wl = W.SMALL_DECODE.replace(name="decode_b3_ctx5000_int_dominant_run", integer_indexer=True, seed=61)
+    announce("fused decode, dominant token run", wl.name)
+    inp = W.generate(wl, "cpu")
+    three = torch.tensor(3.0).to(torch.float8_e4m3fn).view(torch.uint8)
+    inp.q8[:, 0, :] = three                      # head 0: all +3
+    inp.w[:, 0] = 2.0
+    inp.w[:, 1:] = 0.0
+    inp.k8[:, 1000:4000, :] = three              # z = 128 * 9 for these tokens, |z| <= 128 * 9 elsewhere
+    inp.k8[:, :1000, :] = 0
+    inp.k8[:, 4000:, :] = 0
+    _decode_against_staged_and_oracle(inp.to(DEV), wl.name, exact=True)
+
+
+def test_fused_decode_integer_ties():
+    """Integer scores with many exact ties at the k-th key: cut chunks whose
+    smallest kept key ties the k-th key are selected again from the scores."""
+    wl = W.SMALL_DECODE.replace(name="decode_b3_ctx5000_int", integer_indexer=True, seed=62)
+    announce("fused decode, integer ties", wl.name)
+    _decode_against_staged_and_oracle(W.generate(wl, "cpu").to(DEV), wl.name, exact=True)
+
+
 # ------------------------------------------------------------------ fused prefill
 
 @pytest.mark.parametrize("wl", [W.TINY_PREFILL, W.SMALL_PREFILL, W.SMALL_CHUNKED], ids=lambda w: w.name)
