@@ -272,6 +272,20 @@ dsa_status dsa_indexer_warmup(const dsa_batch* batch, const uint16_t* q, const d
 dsa_status dsa_set_attn_splits(int nsplit);
 
 /*
+ * dsa_set_indexer_fp8 — tuning and testing hook for the streaming prefill
+ * (dsa_prefill_streaming) calls that follow on this thread.  1: the filtered
+ * indexer pass contracts the FP8 query and key bytes on the FP8 matrix-core
+ * form (the pages' FP8 lightning indexer: ouchyi.pink post, DSA paragraph;
+ * tenelement.pl "DeepSeek V3.2-Exp Cuts Long-Context Costs", section
+ * "Architektura DeepSeek V3.2-Exp: Od MoE do DSA") and scores exactly only
+ * the pairs whose FP8 score plus its error bound reaches the row threshold;
+ * 0 (the default, the faster one on gfx950): every pair is scored exactly.
+ * The selection is the same either way.
+ * Errors: DSA_ERR_SHAPE if `on` is not 0 or 1.
+ */
+dsa_status dsa_set_indexer_fp8(int on);
+
+/*
  * dsa_decode_noalloc — dsa_decode for callers that cannot allocate device
  * memory: code under HIP graph capture, tight serving loops, harnesses that
  * forbid hipMalloc.  Arguments, results and errors as dsa_decode, without

@@ -26,7 +26,8 @@ from ._lib import (DSA_WS_ATTN, DSA_WS_DECODE, DSA_WS_PREFILL, DSA_WS_PREFILL_ST
                    DSA_WS_TOPK, DSA_WS_WARMUP, DsaBatch, DsaCache)
 
 __all__ = ["Batch", "DsaError", "indexer", "topk", "sparse_attn", "decode", "prefill", "prefill_streaming",
-           "indexer_warmup", "workspace_size", "cache_view", "set_attn_splits"]
+           "indexer_warmup", "workspace_size", "cache_view", "set_attn_splits",
+           "set_indexer_fp8"]
 
 
 class DsaError(RuntimeError):
@@ -106,6 +107,12 @@ def _ref(c):
 def set_attn_splits(nsplit: int) -> None:
     """dsa_set_attn_splits: force the attention split count of later calls on this thread (0 = automatic)."""
     _check(_lib.load().dsa_set_attn_splits(int(nsplit)), "dsa_set_attn_splits")
+
+
+def set_indexer_fp8(on: bool) -> None:
+    """dsa_set_indexer_fp8: FP8 contraction with exact rescoring (True) or exact scoring only (False, the
+    default), for later streaming prefill calls on this thread."""
+    _check(_lib.load().dsa_set_indexer_fp8(1 if on else 0), "dsa_set_indexer_fp8")
 
 
 def workspace_size(entry: int, batch: Batch, k: int, H: int = 0, D_v: int = 0) -> int:

@@ -49,6 +49,7 @@ SIGNATURES = {
     "dsa_workspace_size": ([_I, _BP, _I, _I, _I], _SZ),
     "dsa_set_stage_events": ([ctypes.POINTER(ctypes.c_void_p), _I], _I),
     "dsa_set_attn_splits": ([_I], _I),
+    "dsa_set_indexer_fp8": ([_I], _I),
     "dsa_last_error": ([], ctypes.c_char_p),
 }
 

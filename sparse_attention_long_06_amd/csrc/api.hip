@@ -20,6 +20,7 @@ thread_local hipEvent_t g_stage_events[kMaxStageEvents] = {};
 thread_local int g_stage_count = 0;
 thread_local bool g_stage_armed = false;
 thread_local int g_force_splits = 0;   // dsa_set_attn_splits: 0 = the planner's choice
+thread_local bool g_indexer_fp8 = false;  // dsa_set_indexer_fp8
 
 dsa_status fail(dsa_status s, const char* fmt, ...) {
   char buf[512];
@@ -450,6 +451,12 @@ extern "C" dsa_status dsa_set_attn_splits(int nsplit) {
   return ok();
 }
 
+extern "C" dsa_status dsa_set_indexer_fp8(int on) {
+  CHECK(on == 0 || on == 1, DSA_ERR_SHAPE, "dsa_set_indexer_fp8 takes 0 or 1, got %d", on);
+  g_indexer_fp8 = on == 1;
+  return ok();
+}
+
 extern "C" dsa_status dsa_set_stage_events(void* const* events, int count) {
   if (!events) {
     g_stage_armed = false;
@@ -700,6 +707,7 @@ dsa_status run_stream(const dsa_batch* batch, const uint8_t* q8, const float* q_
     fa.lists = reinterpret_cast<uint2*>(ws + p.off_lists);
     fa.segs = reinterpret_cast<uint2*>(ws + p.off_segs);
     fa.cap = p.cap;
+    fa.fp8 = g_indexer_fp8;
     CHECK((int64_t)fa.nchunks * fa.ntiles < (int64_t)1 << 31, DSA_ERR_UNSUPPORTED, "indexer grid too large");
     LAUNCH(launch_indexer_stream(fa, s), "filtered indexer launch");
   }

@@ -35,6 +35,8 @@ struct IndexerArgs {
   uint2* lists = nullptr;                    // [T, cap] (key, token)
   uint2* segs = nullptr;                     // [T, kStreamMaxSegs] (chunk << 3 | flush, base << 16 | count)
   int cap = 0;
+  // Filtered pass only: decide on FP8 matrix-core scores, keep on exact ones.
+  bool fp8 = false;
 };
 
 // Rows of one workgroup in the prefill layout (4 waves x kIdxRowsPerWave rows).

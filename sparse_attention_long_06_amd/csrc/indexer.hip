@@ -415,11 +415,51 @@ __global__ void __launch_bounds__(256) indexer_decode_ring_kernel(IndexerArgs a)
 // older DMA of the wave, so the ring waits stay correct, only longer, when a
 // flush falls inside the loop.  kshift > 0 runs the kernel over a compacted
 // sample of every 2^kshift-th token (causal bound p >> kshift).
+//
+// F8 (filtered pass only): the scores that decide which pairs are kept come
+// from v_mfma_scale_f32_16x16x128_f8f6f4 on the raw e4m3 bytes (one
+// instruction per 16 heads x 16 keys, 3.3x the measured issue rate of the
+// bf16 form), and only the keys whose FP8 score plus its error bound reaches
+// the row threshold are scored again exactly, with the bf16 arithmetic of the
+// other variants, from the same ring slot.  The FP8 score differs from the
+// exact one by at most kF8ErrRel * 448 * ks * sum_h |w_h qs| max_d |q8_hd|:
+// the matrix core's FP8 dot product is within kF8ErrRel/2 of
+// max_d |q_d| * max_d |k_d| of the exact one (tests pin it at 2^-10), |k8_d|
+// <= 448, ReLU is 1-Lipschitz, and the other half of the budget covers the
+// bf16 path's own fp32 rounding.  So the pairs kept, their keys and the
+// buffer flushes are exactly those of the bf16 filtered pass.
 constexpr int kPreRing = 6;
 constexpr int kPreKeys = 64;
+constexpr float kF8ErrRel = 0x1p-7f;
 
-template <int HT, bool SCALE, bool FILT>
-__global__ void __launch_bounds__(256) indexer_prefill_ring_kernel(IndexerArgs a) {
+// Position of the n-th (from 0) set bit of m; n < popcount(m).
+__device__ __forceinline__ int nth_set_bit(unsigned long long m, int n) {
+  int p = 0;
+#pragma unroll
+  for (int w = 32; w >= 1; w >>= 1) {
+    const int c = __popcll((m >> p) & ((1ull << w) - 1ull));
+    if (n >= c) {
+      n -= c;
+      p += w;
+    }
+  }
+  return p;
+}
+
+// v[g] of four values (selects: an indexed array would go to scratch memory).
+__device__ __forceinline__ float sel4(int g, float v0, float v1, float v2, float v3) {
+  const float lo = (g & 1) ? v1 : v0;
+  const float hi = (g & 1) ? v3 : v2;
+  return (g & 2) ? hi : lo;
+}
+
+__device__ __forceinline__ v8i frag_v8i(const Frag<128>& f) {
+  return v8i{f.lo.x, f.lo.y, f.lo.z, f.lo.w, f.hi.x, f.hi.y, f.hi.z, f.hi.w};
+}
+
+template <int HT, bool SCALE, bool FILT, bool F8 = false>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) indexer_prefill_ring_kernel(IndexerArgs a) {
+  static_assert(!F8 || FILT, "the FP8 contraction serves the filtered pass");
   constexpr int DI = 128;
   constexpr int R = 2;                                // rows per wave
   constexpr int SLOT = kPreKeys * DI + kPreKeys * 4;  // keys + scales
@@ -519,7 +559,9 @@ __global__ void __launch_bounds__(256) indexer_prefill_ring_kernel(IndexerArgs a
   // prologue; the compiler waits for both before the rows are used)
   for (int m = 0; m < kPreRing - 1 && m < nslots; ++m) issue(m);
 
-  Wide<DI> qa[R][HT];
+  Wide<DI> qa[F8 ? 1 : R][F8 ? 1 : HT];
+  Frag<DI> q8[F8 ? R : 1][F8 ? HT : 1];             // F8: the raw query bytes
+  float marg[R];                                      // F8: score error bound per unit key scale
   float wq[R][HT][4];
   int64_t trow[R];
 #pragma unroll
@@ -529,6 +571,7 @@ __global__ void __launch_bounds__(256) indexer_prefill_ring_kernel(IndexerArgs a
     const int t = row0 + (ok ? ri : 0);
     trow[r] = ok ? t : -1;
     const float qs = a.q_scale ? a.q_scale[t] : 1.0f;
+    marg[r] = 0.0f;
 #pragma unroll
     for (int ht = 0; ht < HT; ++ht) {
       const int h = ht * 16 + nl;
@@ -537,7 +580,26 @@ __global__ void __launch_bounds__(256) indexer_prefill_ring_kernel(IndexerArgs a
         load_frag<DI, false>(raw, reinterpret_cast<const char*>(a.q8) + ((int64_t)t * a.H_I + h) * DI, grp);
       else
         zero_frag<DI>(raw);
-      qa[r][ht] = widen<DI>(raw);
+      if constexpr (F8) {
+        q8[r][ht] = raw;
+        // |w_h qs| max_d |q8_hd| of head h, summed over the 16 heads below
+        const Wide<DI> wv = widen<DI>(raw);
+        float mq = 0.0f;
+#pragma unroll
+        for (int c = 0; c < DI / 32; ++c)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) mq = fmaxf(mq, fabsf((float)wv.c[c][e]));
+        mq = fmaxf(mq, __shfl_xor(mq, 16));
+        mq = fmaxf(mq, __shfl_xor(mq, 32));
+        float c = h < a.H_I ? fabsf(a.w[(int64_t)t * a.H_I + h] * qs) * mq : 0.0f;
+        c += __shfl_xor(c, 1);
+        c += __shfl_xor(c, 2);
+        c += __shfl_xor(c, 4);
+        c += __shfl_xor(c, 8);
+        marg[r] += c;
+      } else {
+        qa[r][ht] = widen<DI>(raw);
+      }
       const int hw = ht * 16 + grp * 4;
       const float4 w4 = hw < a.H_I ? *reinterpret_cast<const float4*>(a.w + (int64_t)t * a.H_I + hw)
                                    : make_float4(0.f, 0.f, 0.f, 0.f);
@@ -546,6 +608,9 @@ __global__ void __launch_bounds__(256) indexer_prefill_ring_kernel(IndexerArgs a
       wq[r][ht][2] = w4.z * qs;
       wq[r][ht][3] = w4.w * qs;
     }
+    // the bound on 448 * max|q8| * max|k8| relative terms, inflated by 2^-10
+    // for the rounding of x + margin below
+    if constexpr (F8) marg[r] *= kF8ErrRel * 448.0f * (1.0f + 0x1p-10f);
   }
   // FILT: per row its position (-1: no row), threshold, buffered pairs and
   // the number of segments this workgroup has flushed for it (all uniform)
@@ -633,25 +698,88 @@ __global__ void __launch_bounds__(256) indexer_prefill_ring_kernel(IndexerArgs a
       kf.lo = *reinterpret_cast<const v4i*>(slot + j * 16 * DI + rb0);
       kf.hi = *reinterpret_cast<const v4i*>(slot + j * 16 * DI + rb1);
       const float ks = SCALE ? *reinterpret_cast<const float*>(slot + kPreKeys * DI + 4 * (16 * j + nl)) : 1.0f;
-      const Wide<DI> kb = widen<DI>(kf);
-      const int s = kbeg + m * kPreKeys + 16 * j + nl;
+      if constexpr (F8) {
+        const v8i k8 = frag_v8i(kf);
 #pragma unroll
-      for (int r = 0; r < R; ++r) {
-        float part = 0.0f;
+        for (int r = 0; r < R; ++r) {
+          float part = 0.0f;
 #pragma unroll
-        for (int ht = 0; ht < HT; ++ht) {
-          const v4f acc = mfma_dot<DI>(qa[r][ht], kb);
+          for (int ht = 0; ht < HT; ++ht) {
+            const v4f acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(frag_v8i(q8[r][ht]), k8,
+                                                                              v4f{0.f, 0.f, 0.f, 0.f},
+                                                                              0, 0, 0, 127, 0, 127);
 #pragma unroll
-          for (int i = 0; i < 4; ++i) part = fmaf(wq[r][ht][i], relu(acc[i]), part);
+            for (int i = 0; i < 4; ++i) part = fmaf(wq[r][ht][i], relu(acc[i]), part);
+          }
+          fv[j][r] = group_sum(part) * ks;            // the FP8 estimate of key 16j + nl
         }
-        part = group_sum(part);
-        if constexpr (FILT)
-          fv[j][r] = part * ks;                       // every lane holds the score of key 16j + nl
-        else if (grp == 0 && s < kend && trow[r] >= 0)
-          a.scores[trow[r] * a.ld + s] = part * ks;
+      } else {
+        const Wide<DI> kb = widen<DI>(kf);
+        const int s = kbeg + m * kPreKeys + 16 * j + nl;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          float part = 0.0f;
+#pragma unroll
+          for (int ht = 0; ht < HT; ++ht) {
+            const v4f acc = mfma_dot<DI>(qa[F8 ? 0 : r][F8 ? 0 : ht], kb);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) part = fmaf(wq[r][ht][i], relu(acc[i]), part);
+          }
+          part = group_sum(part);
+          if constexpr (FILT)
+            fv[j][r] = part * ks;                     // every lane holds the score of key 16j + nl
+          else if (grp == 0 && s < kend && trow[r] >= 0)
+            a.scores[trow[r] * a.ld + s] = part * ks;
+        }
       }
     }
-    if constexpr (FILT) {
+    if constexpr (F8) {
+      // lane l takes key l of the slot; the keys whose FP8 estimate plus its
+      // bound reaches the row threshold are scored exactly in batches of 16
+      // (column n of a batch: the (16b + n)-th such key, so token order is
+      // kept) and appended when their exact (key, token) order reaches it
+      const int sl = kbeg + m * kPreKeys + lane;
+      const float ksl = SCALE ? *reinterpret_cast<const float*>(slot + kPreKeys * DI + 4 * lane) : 1.0f;
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const float xt = sel4(grp, fv[0][r], fv[1][r], fv[2][r], fv[3][r]);
+        const bool maybe = sl <= rpos[r] && score_key(xt + marg[r] * fabsf(ksl)) >= (uint32_t)(rthr[r] >> 32);
+        const unsigned long long mm = __ballot(maybe);
+        const int cnt = __popcll(mm);
+        for (int b0 = 0; b0 < cnt; b0 += 16) {
+          const int n = b0 + nl;
+          const int q = nth_set_bit(mm, n < cnt ? n : cnt - 1);
+          const int kq = q & 15;
+          const char* krow = slot + (q >> 4) * 16 * DI + kq * DI;
+          Frag<DI> kf;
+          kf.lo = *reinterpret_cast<const v4i*>(krow + 16 * ((2 * grp) ^ kswz(kq)));
+          kf.hi = *reinterpret_cast<const v4i*>(krow + 16 * ((2 * grp + 1) ^ kswz(kq)));
+          const float ks = SCALE ? *reinterpret_cast<const float*>(slot + kPreKeys * DI + 4 * q) : 1.0f;
+          const Wide<DI> kb = widen<DI>(kf);
+          float part = 0.0f;
+#pragma unroll
+          for (int ht = 0; ht < HT; ++ht) {
+            // widened here, per batch: kept widened (loop-invariant, so the
+            // compiler would hoist it) it would cost 128 more registers
+            Frag<DI> qr = q8[r][ht];
+            asm volatile("" : "+v"(qr.lo), "+v"(qr.hi));
+            const v4f acc = mfma_dot<DI>(widen<DI>(qr), kb);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) part = fmaf(wq[r][ht][i], relu(acc[i]), part);
+          }
+          const float x = group_sum(part) * ks;
+          const int sq = kbeg + m * kPreKeys + q;
+          const uint32_t key = score_key(x);
+          const unsigned long long comp = ((unsigned long long)key << 32) | (uint32_t)~(uint32_t)sq;
+          const bool keep = grp == 0 && n < cnt && comp >= rthr[r];
+          const unsigned long long k64 = __ballot(keep);
+          const uint32_t before = __builtin_amdgcn_mbcnt_hi((uint32_t)(k64 >> 32),
+                                                            __builtin_amdgcn_mbcnt_lo((uint32_t)k64, 0u));
+          if (keep) mycand[r * kStreamLds + ccnt[r] + before] = make_uint2(key, (uint32_t)sq);
+          ccnt[r] += (uint32_t)__popcll(k64);
+        }
+      }
+    } else if constexpr (FILT) {
       // lane (g, l) takes key 16g + l of the slot, so the 64 lanes hold the
       // slot's keys in token order: one ballot and one append per row keep
       // (key, token) when token <= p and (key, ~token) reaches the threshold
@@ -713,8 +841,13 @@ static hipError_t launch_di(const IndexerArgs& a, bool decode_layout, bool with_
 template <int HT>
 static hipError_t launch_stream_ht(const IndexerArgs& a, hipStream_t s) {
   const dim3 grid(a.nchunks * a.ntiles, 1, a.g.num_seqs);
-  if (a.ksc.data) hipLaunchKernelGGL((indexer_prefill_ring_kernel<HT, true, true>), grid, dim3(256), 0, s, a);
-  else hipLaunchKernelGGL((indexer_prefill_ring_kernel<HT, false, true>), grid, dim3(256), 0, s, a);
+  if (a.fp8) {
+    if (a.ksc.data) hipLaunchKernelGGL((indexer_prefill_ring_kernel<HT, true, true, true>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((indexer_prefill_ring_kernel<HT, false, true, true>), grid, dim3(256), 0, s, a);
+  } else {
+    if (a.ksc.data) hipLaunchKernelGGL((indexer_prefill_ring_kernel<HT, true, true>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((indexer_prefill_ring_kernel<HT, false, true>), grid, dim3(256), 0, s, a);
+  }
   return hipGetLastError();
 }
 

@@ -25,7 +25,7 @@ def lib():
 def _declared():
     txt = open(HEADER).read()
     txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
-    return sorted(set(re.findall(r"\b(dsa_[a-z_]+)\s*\(", txt)))
+    return sorted(set(re.findall(r"\b(dsa_[a-z0-9_]+)\s*\(", txt)))
 
 
 def test_header_declares_the_four_calls():
@@ -140,6 +140,13 @@ def test_stage_events_validation(lib):
     assert lib.dsa_set_stage_events(ev, 3) == _lib.DSA_ERR_SHAPE
     assert lib.dsa_set_stage_events(ev, 4) == _lib.DSA_ERR_NULL
     assert lib.dsa_set_stage_events(None, 0) == _lib.DSA_OK
+
+
+def test_indexer_fp8_switch_validation(lib):
+    assert lib.dsa_set_indexer_fp8(2) == _lib.DSA_ERR_SHAPE
+    assert "0 or 1" in _err(lib)
+    assert lib.dsa_set_indexer_fp8(0) == _lib.DSA_OK
+    assert lib.dsa_set_indexer_fp8(1) == _lib.DSA_OK
 
 
 def test_prefill_validation(lib):

@@ -105,6 +105,32 @@ def test_streaming_equals_prefill_and_oracle(wl):
     _oracle_check(inp, idx, out, lse, rows, exact=wl.integer_indexer)
 
 
+FP8_CASES = [CASES[1], CASES[4], CASES[6], CASES[8]]
+
+
+@pytest.mark.parametrize("wl", FP8_CASES, ids=[w.name for w in FP8_CASES])
+def test_fp8_filter_equals_exact_filter(wl):
+    """The filtered pass decides on FP8 matrix-core scores plus their error
+    bound and keeps on exact ones (dsa_set_indexer_fp8(1)), or scores every
+    pair exactly (0, the default).  The kept pairs, hence the selection and
+    the attention over it, must be the same bit for bit."""
+    announce("fp8 filter vs exact filter", wl.name)
+    inp = W.generate(wl, DEV)
+    batch = dsa.Batch.from_inputs(inp)
+    res = []
+    try:
+        for on in (False, True):
+            dsa.set_indexer_fp8(on)
+            idx = torch.empty((inp.num_rows, wl.k), dtype=torch.int32, device=DEV)
+            out, lse, _ = dsa.prefill_streaming(batch, inp.q8, inp.q_scale, inp.w, inp.k8, inp.k_scale, wl.k,
+                                                inp.q, inp.kv, inp.v, wl.scale, idx_out=idx, D_v=wl.D_v)
+            torch.cuda.synchronize()
+            res.append((idx, out, lse))
+    finally:
+        dsa.set_indexer_fp8(False)
+    _assert_same(res[0], res[1], wl.name + " fp8")
+
+
 def test_streaming_chunked_prefill_late_chunk():
     """A chunk whose rows sit at positions 7500..9999 of a growing cache."""
     wl = W.CHUNKED_128K.replace(name="chunked_prefill_L10000_c2500", seq_len=10000, chunk=2500, seed=35,
