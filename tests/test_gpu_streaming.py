@@ -110,25 +110,22 @@ FP8_CASES = [CASES[1], CASES[4], CASES[6], CASES[8]]
 
 @pytest.mark.parametrize("wl", FP8_CASES, ids=[w.name for w in FP8_CASES])
 def test_fp8_filter_equals_exact_filter(wl):
-    """The filtered pass decides on FP8 matrix-core scores plus their error
-    bound and keeps on exact ones (dsa_set_indexer_fp8(1)), or scores every
-    pair exactly (0, the default).  The kept pairs, hence the selection and
-    the attention over it, must be the same bit for bit."""
-    announce("fp8 filter vs exact filter", wl.name)
+    """With dsa_set_indexer_fp8(1) the filtered pass decides on FP8
+    matrix-core scores plus their error bound and keeps on exact ones (the
+    16x16x32 kernels' arithmetic, which every prefill pass of the call then
+    uses).  Its kept pairs, hence the selection and the attention over it,
+    must equal the stored-score path's bit for bit, and the oracle's."""
+    announce("fp8 filter vs stored scores", wl.name)
     inp = W.generate(wl, DEV)
-    batch = dsa.Batch.from_inputs(inp)
-    res = []
     try:
-        for on in (False, True):
-            dsa.set_indexer_fp8(on)
-            idx = torch.empty((inp.num_rows, wl.k), dtype=torch.int32, device=DEV)
-            out, lse, _ = dsa.prefill_streaming(batch, inp.q8, inp.q_scale, inp.w, inp.k8, inp.k_scale, wl.k,
-                                                inp.q, inp.kv, inp.v, wl.scale, idx_out=idx, D_v=wl.D_v)
-            torch.cuda.synchronize()
-            res.append((idx, out, lse))
+        dsa.set_indexer_fp8(True)
+        p, s = _both(inp)
     finally:
         dsa.set_indexer_fp8(False)
-    _assert_same(res[0], res[1], wl.name + " fp8")
+    _assert_same(p, s, wl.name + " fp8")
+    idx, out, lse = (to_np(x) for x in s)
+    rows = W.sample_rows(wl, inp.num_rows, 12, always=(0, wl.k, inp.num_rows - 1))
+    _oracle_check(inp, idx, out, lse, rows, exact=wl.integer_indexer)
 
 
 def test_streaming_chunked_prefill_late_chunk():
