@@ -39,9 +39,9 @@ INDEXER_COUNTERS = {
     "sources": ["sparse_attention_long_06_amd/csrc/indexer.hip", "sparse_attention_long_06_amd/csrc/idx_math.h",
                 "sparse_attention_long_06_amd/csrc/dsa_common.h", "sparse_attention_long_06_amd/csrc/dsa_kernels.h",
                 "sparse_attention_long_06_amd/csrc/api.hip"],
-    "sha256": "5fb3e49894e3840f547e4ba0aecff93237bd3439c42e88c16aef01832acfc9bd",
-    "fetch_kib": 272779.8,
-    "write_kib": 17230.3,
+    "sha256": "bedadf471032f0a17fbb539ae0daf478a6df207d1dd9637e29fb2b9f29085b3c",
+    "fetch_kib": 272869.2,
+    "write_kib": 16384.0,
     "fetch_scale": 2.0,
     "write_scale": 1.0,
 }
@@ -328,7 +328,7 @@ def run_bench(args, workload=None, separate_calls=True, attainable=True):
                    "parallelism": "single GPU"},
         "tokens_per_s": round(qps, 1),
         "context_tokens_scanned_per_s": round(ctx_total / (elapsed / args.steps), 1),
-        "roofline": {"bound": "hbm", "kernel": "indexer_decode_ring_kernel (decode indexer + first top-k histogram)",
+        "roofline": {"bound": "hbm", "kernel": "indexer_decode_ring_kernel (decode indexer: FP8 keys, scores)",
                      "achieved": round(idx_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(idx_gbs / HBM_PEAK_GBS, 4), "traffic": indexer_traffic_bytes(wl.name),
                      "bytes_per_launch": idx_bytes, "launch_ms": round(stage_ms["indexer"], 4)},
