@@ -355,9 +355,15 @@ __global__ void __launch_bounds__(512) attn_kernel(AttnArgs a) {
 //     operands).  Lane l then holds dims 8(i/4) + 4(l/32) + i%4 of every
 //     32-dim tile of head l%32 only: a head's rescale and final 1/l are the
 //     lane's own factors, with no exchange;
-//   * 16-byte chunk c of row r sits at chunk (c & ~7) | ((c & 7) ^ f(r)),
-//     f(r) = ((r>>1 & 1) << 2) | (r>>2 & 3): the 16 rows of a K read and the
-//     4 rows x 4 chunks of a half-wave's V read land in distinct bank groups.
+//   * a tile is stored in nine blocks of 8 chunks (128 bytes of each row):
+//     16-byte chunk c of row r sits at byte 4096 (c/8) + 128 r +
+//     16 ((c%8) ^ f(r)), f(r) = ((r>>1 & 1) << 2) | (r>>2 & 3), so the 16
+//     rows of a K read and the 4 rows x 4 chunks of a half-wave's V read land
+//     in distinct bank groups.  DMA instruction 4m + w fills block m for rows
+//     8w..8w+7: 8 whole 128-byte lines, one per row, and a lane fetches the
+//     same row at the same in-block position for every m, so a tile costs one
+//     row-id read and one 64-bit address per lane, the block as an immediate
+//     offset.
 constexpr int kWideRows = 32;       // selected rows per tile
 constexpr int kWideSlots = 4;       // tiles in the LDS ring (three in flight while one is computed)
 constexpr int kWideWaves = 4;       // 32 heads each
@@ -407,39 +413,34 @@ attn_wide_kernel(AttnArgs a) {
   const int h0 = wave * 32;
 
   const uint32_t ring = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)&tiles[0][0];
-  // DMA of 32 rows into ring slot `slot`: row rid(r) of `base` (rows
-  // row_stride bytes apart), 16-byte chunk c of row r to chunk
-  // (c & ~7) | ((c & 7) ^ f(r)); instruction ins fills LDS bytes
-  // [1024 ins, 1024 ins + 1024) of the slot.  This call issues instructions
-  // ins0, ins0 + 4, ... (NIW of them).  The per-lane offsets are recomputed
-  // each time (an opaque copy of the lane id keeps them from being hoisted
-  // into long-lived VGPRs); the row ids are all fetched before the first DMA
-  // is issued, so their latencies overlap.
-  auto dma_rows = [&](int slot, const char* base, int64_t row_stride, auto rid, int ins0) {
-    const uint32_t lds0 = ring + (uint32_t)(slot * TILE);
-    int ln = lane;
-    asm volatile("" : "+v"(ln));
-    uint32_t row[NIW];
-    int chk[NIW];
-#pragma unroll
-    for (int m = 0; m < NIW; ++m) {
-      const int p = (ins0 + kWideWaves * m) * 64 + ln;
-      const int r = p / CH, pc = p % CH;
-      chk[m] = (pc & ~7) | ((pc & 7) ^ wswz(r));
-      row[m] = rid(r);
-    }
-#pragma unroll
-    for (int m = 0; m < NIW; ++m) {
-      const int ins = ins0 + kWideWaves * m;
-      const char* src = base + (int64_t)row[m] * row_stride + chk[m] * 16;
-      const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds0 + ins * 1024);
-      asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" :: "s"(m0), "v"(src) : "memory");
-    }
+  // DMA instructions ins0, ins0 + 4, ..., ins0 + 32 of a tile into ring slot
+  // `slot`: instruction ins0 + 4m fills slot bytes [1024 (ins0 + 4m), +1024),
+  // block m of rows 8 ins0..8 ins0 + 7.  `row` is the source row of this lane
+  // (tile row 8 ins0 + l/8; its offset in rows of row_stride bytes from base),
+  // the same for all nine.  The instruction's immediate offset (128 m) moves
+  // the LDS destination as well as the global address, so M0 is set 128 m
+  // below the destination: 1024 ins0 + 3968 m.
+  const int drow = lane >> 3;
+  auto dma_rows = [&](int slot, const char* base, int64_t row_stride, uint32_t row, int ins0) {
+    static_assert(NIW == 9, "nine DMA instructions per wave and tile");
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane(ring + (uint32_t)(slot * TILE + ins0 * 1024));
+    const char* src = base + (int64_t)row * row_stride + 16 * ((lane & 7) ^ wswz(8 * ins0 + drow));
+    asm volatile(
+        "s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off\n\t"
+        "s_add_u32 m0, %0, 3968\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off offset:128\n\t"
+        "s_add_u32 m0, %0, 7936\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off offset:256\n\t"
+        "s_add_u32 m0, %0, 11904\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off offset:384\n\t"
+        "s_add_u32 m0, %0, 15872\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off offset:512\n\t"
+        "s_add_u32 m0, %0, 19840\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off offset:640\n\t"
+        "s_add_u32 m0, %0, 23808\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off offset:768\n\t"
+        "s_add_u32 m0, %0, 27776\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off offset:896\n\t"
+        "s_add_u32 m0, %0, 31744\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off offset:1024"
+        :: "s"(m0), "v"(src) : "memory", "m0", "scc");
   };
   // tile `tile` of the selected rows: the four waves share its DMA instructions
   auto gather = [&](int tile) {
-    const uint32_t* rid = rowid + tile * kWideRows;
-    dma_rows(tile % kWideSlots, a.kv.data, a.kv.row_stride, [&](int r) { return rid[r]; }, wave);
+    const uint32_t row = rowid[tile * kWideRows + 8 * wave + drow];
+    dma_rows(tile % kWideSlots, a.kv.data, a.kv.row_stride, row, wave);
   };
 
   // Prologue.  The q block of this wave (heads h0..h0+31: 36,864 contiguous
@@ -450,7 +451,7 @@ attn_wide_kernel(AttnArgs a) {
     const char* qblock = reinterpret_cast<const char*>(a.q + ((int64_t)t * a.H + h0) * D);
 #pragma unroll
     for (int part = 0; part < kWideWaves; ++part)
-      dma_rows(wave, qblock, (int64_t)D * 2, [](int r) { return (uint32_t)r; }, part);
+      dma_rows(wave, qblock, (int64_t)D * 2, (uint32_t)(8 * part + drow), part);
   }
   int b, pos;
   row_seq_pos(a.g, t, b, pos);
@@ -475,23 +476,13 @@ attn_wide_kernel(AttnArgs a) {
   // q fragments (B operand of S^T): head h0 + n32, dims 16kk + 8g .. +7, from
   // this wave's own staging slot (its DMA is complete after vmcnt(0))
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  v8bf qf[KK];
-  {
-    const char* qs = &tiles[wave][0];
-    const int y = wswz(n32);
-#pragma unroll
-    for (int kk = 0; kk < KK; ++kk)
-      qf[kk] = *reinterpret_cast<const v8bf*>(qs + n32 * CH * 16 + (kk >> 2) * 128 + 16 * ((2 * (kk & 3) + g) ^ y));
-  }
-  __syncthreads();        // row ids published; every wave holds its q (the slots are free again)
-
-  // per-lane LDS operand offsets within a tile
+  // per-lane LDS operand offsets within a tile.  K (and q): row n32, chunk
+  // 2kk + g at byte 4096 (kk/4) + kb[kk%4].  V^T: lane i of 16-lane group G
+  // reads row 16u + 8h + 4(G/2) + i/4, chunk 4nt + 2(G&1) + (i/2 & 1), half
+  // i&1, at byte 4096 (nt/2) + 2048 u + vb[h][nt&1].
   int kb[4];
-  {
-    const int y = wswz(n32);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) kb[q] = n32 * CH * 16 + 16 * ((2 * q + g) ^ y);
-  }
+  for (int q = 0; q < 4; ++q) kb[q] = 128 * n32 + 16 * ((2 * q + g) ^ wswz(n32));
   int vb[2][2];
   {
     const int G = lane >> 4, i = lane & 15;
@@ -501,9 +492,16 @@ attn_wide_kernel(AttnArgs a) {
       const int y = wswz(row);
 #pragma unroll
       for (int np = 0; np < 2; ++np)
-        vb[h][np] = row * CH * 16 + 16 * ((4 * np + 2 * (G & 1) + ((i & 3) >> 1)) ^ y) + 8 * (i & 1);
+        vb[h][np] = 128 * row + 16 * ((4 * np + 2 * (G & 1) + ((i & 3) >> 1)) ^ y) + 8 * (i & 1);
     }
   }
+  v8bf qf[KK];
+  {
+    const char* qs = &tiles[wave][0];
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) qf[kk] = *reinterpret_cast<const v8bf*>(qs + 4096 * (kk >> 2) + kb[kk & 3]);
+  }
+  __syncthreads();        // row ids published; every wave holds its q (the slots are free again)
 
   v16f o[NT];
 #pragma unroll
@@ -533,7 +531,7 @@ attn_wide_kernel(AttnArgs a) {
     constexpr int KD = 4, KR = 6;
     v16f sa, sb;
     v8bf kr[KR];
-    auto kread = [&](int kk) -> v8bf { return *reinterpret_cast<const v8bf*>(kt + kb[kk & 3] + (kk >> 2) * 128); };
+    auto kread = [&](int kk) -> v8bf { return *reinterpret_cast<const v8bf*>(kt + 4096 * (kk >> 2) + kb[kk & 3]); };
 #pragma unroll
     for (int kk = 0; kk < KD; ++kk) kr[kk] = kread(kk);
 #pragma unroll
@@ -557,7 +555,7 @@ attn_wide_kernel(AttnArgs a) {
     // softmax; P V runs all dim tiles of k-step u = 0 (rows 0-15), then u = 1
     auto vread = [&](int st) -> v8bf {
       const int nt = st & (NT - 1), u = st / NT;
-      const char* p0 = kt + u * 16 * CH * 16 + (nt >> 1) * 128;
+      const char* p0 = kt + 4096 * (nt >> 1) + 2048 * u;
       const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(p0 + vb[0][nt & 1]));
       const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(p0 + vb[1][nt & 1]));
       return __builtin_bit_cast(v8bf, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
