@@ -510,26 +510,21 @@ attn_wide_kernel(AttnArgs a) {
     for (int i = 0; i < 16; ++i) o[nt][i] = 0.0f;
   float m_run = -INFINITY, l_run = 0.0f;   // head n32: running max (log2 units) and this lane's partial sum
 
-  // One tile: wait for its DMA, S^T = K q^T, online softmax, O^T += V^T P^T.
-  auto step = [&](int j) {
-    // wait for tile j: the tiles after it (up to two) may stay in flight
-    if (j + 2 < ntiles) asm volatile("s_waitcnt vmcnt(%0)" :: "n"(2 * NIW) : "memory");
-    else if (j + 1 < ntiles) asm volatile("s_waitcnt vmcnt(%0)" :: "n"(NIW) : "memory");
-    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();        // tile j is in LDS; every wave is done with tile j-1
-    if (j + kWideSlots - 1 < ntiles) gather(j + kWideSlots - 1);
-    const char* kt = &tiles[j % kWideSlots][0];
-
-    // ---- S^T = K q^T over 36 k-steps, two accumulator chains in VGPRs
-    // (even and odd k-steps).  Written as inline asm so the accumulators stay
-    // in VGPRs and the output accumulators keep all 256 AGPRs.  Each chain
-    // starts from a zero SrcC and accumulates in place (SrcC = VDST, same
-    // shape); the last pair is followed by enough wait states (21) for VALU
-    // reads of an XDL result, which the compiler does not insert after inline
-    // asm.  With one wave per SIMD only the wave's own prefetch hides the LDS
-    // latency: K fragments are read four steps ahead through a 6-entry ring.
+  // ---- S^T = K q^T of tile jt over 36 k-steps, two accumulator chains in
+  // VGPRs (even and odd k-steps; one chain of dependent matrix-core
+  // instructions runs at about half the rate).  Written as inline asm so the
+  // accumulators stay in VGPRs and the output accumulators keep all 256
+  // AGPRs.  Each chain starts from a zero SrcC and accumulates in place
+  // (SrcC = VDST, same shape); the last pair is followed by enough wait states
+  // (21) for VALU reads of an XDL result, which the compiler does not insert
+  // after inline asm.  With one wave per SIMD only the wave's own prefetch
+  // hides the LDS latency: K fragments are read four steps ahead through a
+  // 6-entry ring.  work(kk) runs after the instruction of step kk: VALU work
+  // of the previous tile's softmax, which then overlaps the matrix core.
+  v16f sa, sb;
+  auto s_tile = [&](int jt, auto&& work) {
+    const char* kt = &tiles[jt % kWideSlots][0];
     constexpr int KD = 4, KR = 6;
-    v16f sa, sb;
     v8bf kr[KR];
     auto kread = [&](int kk) -> v8bf { return *reinterpret_cast<const v8bf*>(kt + 4096 * (kk >> 2) + kb[kk & 3]); };
 #pragma unroll
@@ -548,50 +543,71 @@ attn_wide_kernel(AttnArgs a) {
         asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0\n\ts_nop 7\n\ts_nop 7\n\ts_nop 4"
                      : "+v"(sb) : "v"(k0), "v"(qf[kk]));
       }
+      work(kk);
       __builtin_amdgcn_sched_barrier(0);
     }
+  };
 
-    // the first V fragments of the P V product are requested before the
-    // softmax; P V runs all dim tiles of k-step u = 0 (rows 0-15), then u = 1
-    auto vread = [&](int st) -> v8bf {
-      const int nt = st & (NT - 1), u = st / NT;
-      const char* p0 = kt + 4096 * (nt >> 1) + 2048 * u;
-      const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(p0 + vb[0][nt & 1]));
-      const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(p0 + vb[1][nt & 1]));
-      return __builtin_bit_cast(v8bf, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-    };
-    constexpr int VD = 4, VR = 6;
-    v8bf vr[VR];
+  // Software pipeline over the tiles: iteration j takes S^T of tile j (from
+  // the accumulators), computes S^T of tile j+1 on the matrix core while the
+  // VALU does the online softmax of tile j in its shadow, then O^T += V^T P^T
+  // for tile j.  Iteration j reads tiles j (V) and j+1 (K); tiles j+2 and j+3
+  // are in flight, and the gather of tile j+3 goes to the slot of tile j-1,
+  // which every wave has finished with at the barrier of iteration j.
 #pragma unroll
-    for (int st = 0; st < VD; ++st) vr[st] = vread(st);
-
-    // ---- online softmax in log2 units (lazily moved reference max, P < 2^8)
-    const uint32_t vm = vmask[j] >> (4 * g);      // bit 8(i/4) + i%4: row of accumulator i
+  for (int j0 = 0; j0 < kWideSlots - 1; ++j0)
+    if (j0 < ntiles) gather(j0);
+  if (ntiles > 0) {
+    if (ntiles > 2) asm volatile("s_waitcnt vmcnt(%0)" :: "n"(2 * NIW) : "memory");
+    else if (ntiles > 1) asm volatile("s_waitcnt vmcnt(%0)" :: "n"(NIW) : "memory");
+    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();        // tile 0 is in LDS
+    s_tile(0, [](int) {});
+  }
+  for (int j = 0; j < ntiles; ++j) {
+    // ---- online softmax of tile j in log2 units (lazily moved reference max,
+    // P < 2^8), spread over the k-steps of the next tile's S^T
     float x[16];
-    float mx = -INFINITY;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      x[i] = ((vm >> (8 * (i >> 2) + (i & 3))) & 1u) ? (sa[i] + sb[i]) * a.scale_log2 : -INFINITY;
-      mx = fmaxf(mx, x[i]);
-    }
-    mx = xhalf_max(mx);
-    const float m_old = m_run;
-    const bool move = mx > m_old + 8.0f;
-    const float m_ref = move ? mx : m_old;
-    const float m_use = (m_ref == -INFINITY) ? 0.0f : m_ref;
-    const float alpha = (move && m_old != -INFINITY) ? __builtin_amdgcn_exp2f(m_old - m_ref) : 1.0f;
-    m_run = m_ref;
-    // P of k-step 0 (accumulators 0-7) now; that of k-step 1 is computed one
-    // value per step inside the first half of the P V loop, where its VALU
-    // work overlaps the matrix core
+    for (int i = 0; i < 16; ++i) x[i] = sa[i] + sb[i];
+    const uint32_t vm = vmask[j] >> (4 * g);      // bit 8(i/4) + i%4: row of accumulator i
+    float mx = -INFINITY, m_use = 0.0f, alpha = 1.0f, psum = 0.0f;
     v8bf pa[2];
-    float psum = 0.0f;
+    auto softmax = [&](int kk) {
+      if (kk < 16) {                // scale and mask one value, running max
+        const int i = kk;
+        x[i] = ((vm >> (8 * (i >> 2) + (i & 3))) & 1u) ? x[i] * a.scale_log2 : -INFINITY;
+        mx = fmaxf(mx, x[i]);
+      } else if (kk == 16) {        // the head's max over both lane halves; move the reference
+        mx = xhalf_max(mx);
+        const float m_old = m_run;
+        const bool move = mx > m_old + 8.0f;
+        const float m_ref = move ? mx : m_old;
+        m_use = (m_ref == -INFINITY) ? 0.0f : m_ref;
+        alpha = (move && m_old != -INFINITY) ? __builtin_amdgcn_exp2f(m_old - m_ref) : 1.0f;
+        m_run = m_ref;
+      } else if (kk < 33) {         // one probability, rounded to bf16
+        const int i = kk - 17;
+        const float pr = __builtin_amdgcn_exp2f(x[i] - m_use);
+        psum += pr;
+        pa[i >> 3][i & 7] = (__bf16)pr;
+      } else if (kk == 33) {
+        l_run = l_run * alpha + psum;
+      }
+    };
+    if (j + 1 < ntiles) {
+      // wait for tile j+1; tile j+2 may stay in flight
+      if (j + 2 < ntiles) asm volatile("s_waitcnt vmcnt(%0)" :: "n"(NIW) : "memory");
+      else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();      // tile j+1 is in LDS; every wave is done with tile j-1
+      if (j + kWideSlots - 1 < ntiles) gather(j + kWideSlots - 1);
+      s_tile(j + 1, softmax);
+    } else {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float p = __builtin_amdgcn_exp2f(x[i] - m_use);
-      psum += p;
-      pa[0][i] = (__bf16)p;
+      for (int kk = 0; kk < KK; ++kk) softmax(kk);
     }
+    const char* kt = &tiles[j % kWideSlots][0];
+
     // ---- rescale O^T where the head's reference moved (lane l holds head l%32
     // only, so the factor is the lane's own).  In place in the accumulation
     // registers, by inline asm so the accumulators never leave them; wait
@@ -627,26 +643,26 @@ attn_wide_kernel(AttnArgs a) {
       }
     }
 
-    // ---- O^T += V^T P^T, V read transposed from the same tile; steps st =
-    // 16u + nt, V fragments four steps ahead through a 6-entry ring
+    // ---- O^T += V^T P^T for tile j, V read transposed from its tile; steps
+    // st = 16u + nt, V fragments four steps ahead through a 6-entry ring
+    auto vread = [&](int st) -> v8bf {
+      const int nt = st & (NT - 1), u = st / NT;
+      const char* p0 = kt + 4096 * (nt >> 1) + 2048 * u;
+      const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(p0 + vb[0][nt & 1]));
+      const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(p0 + vb[1][nt & 1]));
+      return __builtin_bit_cast(v8bf, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    };
+    constexpr int VD = 4, VR = 6;
+    v8bf vr[VR];
+#pragma unroll
+    for (int st = 0; st < VD; ++st) vr[st] = vread(st);
 #pragma unroll
     for (int st = 0; st < 2 * NT; ++st) {
       if (st + VD < 2 * NT) vr[(st + VD) % VR] = vread(st + VD);
-      if (st < 8) {
-        const float p = __builtin_amdgcn_exp2f(x[8 + st] - m_use);
-        psum += p;
-        pa[1][st] = (__bf16)p;
-      }
-      if (st == 8) l_run = l_run * alpha + psum;
       o[st & (NT - 1)] = mfma32(vr[st % VR], pa[st / NT], o[st & (NT - 1)]);
       __builtin_amdgcn_sched_barrier(0);
     }
-  };
-
-#pragma unroll
-  for (int j0 = 0; j0 < kWideSlots - 1; ++j0)
-    if (j0 < ntiles) gather(j0);
-  for (int j = 0; j < ntiles; ++j) step(j);
+  }
 
   // ---- finish: denominator of the lane's head, normalise, write.  Lane l
   // holds dims 32nt + 8q + 4g + i (i < 4) of head h0 + l%32; one permlane32
