@@ -443,33 +443,70 @@ attn_wide_kernel(AttnArgs a) {
     dma_rows(tile % kWideSlots, a.kv.data, a.kv.row_stride, row, wave);
   };
 
-  // Prologue.  The q block of this wave (heads h0..h0+31: 36,864 contiguous
-  // bytes) goes to slot `wave` first (all 36 of its DMA instructions are
-  // this wave's); then the selected token ids and their row ids, whose wait
-  // also covers the q DMA (issued earlier, completing in order).
-  {
-    const char* qblock = reinterpret_cast<const char*>(a.q + ((int64_t)t * a.H + h0) * D);
-#pragma unroll
-    for (int part = 0; part < kWideWaves; ++part)
-      dma_rows(wave, qblock, (int64_t)D * 2, (uint32_t)(8 * part + drow), part);
-  }
+  // Prologue.  Vector-memory loads complete in order, so a load queued behind
+  // the 147 KB q DMA would wait for all of it: the row's sequence and
+  // position are read first, then the split's selected token ids (and, for
+  // paged caches, their block ids) come into rowid[] by LDS DMA ahead of q,
+  // and the token rows are formed from LDS while q is in flight.
   int b, pos;
   row_seq_pos(a.g, t, b, pos);
   const int slot_beg = split * a.per_split;
   const int nslots = min(a.k, slot_beg + a.per_split) - slot_beg;
   const int ntiles = (nslots + kWideRows - 1) / kWideRows;
   const int32_t* sel = a.idx + (int64_t)t * a.k + slot_beg;
-  // token rows of the split's slots (invalid slots borrow token 0 of the
-  // sequence: finite values, zero weight) and one validity bit per slot
+  // invalid slots borrow token 0 of the sequence (finite values, zero weight)
   const uint32_t fallback = (uint32_t)token_row(a.g, a.kv, b, 0);
+  asm volatile("" :: "v"(fallback), "v"(pos));    // those loads are complete before any DMA is queued
+  const uint32_t rid_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)&rowid[0];
+  // 4-byte LDS DMA of this lane's word for slot i = 256 m + 64 wave + lane into rowid[i]
+  auto dma_slot = [&](int m, const void* src) {
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane(rid_lds + 4u * (uint32_t)(64 * kWideWaves * m + 64 * wave));
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off" :: "s"(m0), "v"(src) : "memory", "m0");
+  };
+#pragma unroll
+  for (int m = 0; m < SPT; ++m) {
+    const int i = threadIdx.x + m * 64 * kWideWaves;
+    if (i < nslots) dma_slot(m, sel + i);
+  }
+  int sv[SPT];          // paged: the slots' token ids, kept while their block ids arrive
+  if (a.g.block_table) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");      // only the id DMA is outstanding
+#pragma unroll
+    for (int m = 0; m < SPT; ++m) {
+      const int i = threadIdx.x + m * 64 * kWideWaves;
+      int sm = i < nslots ? (int)rowid[i] : -1;
+      if (sm > pos) sm = -1;
+      sv[m] = sm;
+      if (sm >= 0) dma_slot(m, a.g.block_table + (int64_t)b * a.g.max_blocks + (sm >> a.g.block_shift));
+    }
+  }
+  // this wave's q block (heads h0..h0+31: 36,864 contiguous bytes) into slot `wave`
+  {
+    const char* qblock = reinterpret_cast<const char*>(a.q + ((int64_t)t * a.H + h0) * D);
+#pragma unroll
+    for (int part = 0; part < kWideWaves; ++part)
+      dma_rows(wave, qblock, (int64_t)D * 2, (uint32_t)(8 * part + drow), part);
+  }
+  // at most the 36 q instructions outstanding: this lane's id (block id)
+  // words are in LDS.  Each slot's word was fetched by the lane that now
+  // reads and replaces it with the token row; one validity bit per slot.
+  asm volatile("s_waitcnt vmcnt(%0)" :: "n"(kWideWaves * NIW) : "memory");
 #pragma unroll
   for (int m = 0; m < SPT; ++m) {
     const int i = threadIdx.x + m * 64 * kWideWaves;
     if (i < ntiles * kWideRows) {           // whole waves: ntiles * 32 is a multiple of 32
-      int s = i < nslots ? sel[i] : -1;
-      if (s > pos) s = -1;
-      rowid[i] = s >= 0 ? (uint32_t)token_row(a.g, a.kv, b, s) : fallback;
-      const uint64_t bal = __ballot(s >= 0);
+      int sm;
+      uint32_t row;
+      if (a.g.block_table) {
+        sm = sv[m];
+        row = sm >= 0 ? (rowid[i] << a.g.block_shift) + (uint32_t)(sm & ((1 << a.g.block_shift) - 1)) : fallback;
+      } else {
+        sm = i < nslots ? (int)rowid[i] : -1;
+        if (sm > pos) sm = -1;
+        row = sm >= 0 ? (uint32_t)((int64_t)b * a.kv.seq_stride + sm) : fallback;
+      }
+      rowid[i] = row;
+      const uint64_t bal = __ballot(sm >= 0);
       if ((i & 31) == 0) vmask[i >> 5] = (uint32_t)(bal >> (lane & 32));
     }
   }
