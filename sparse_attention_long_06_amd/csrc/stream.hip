@@ -141,7 +141,9 @@ __global__ void __launch_bounds__(kThrNT) stream_threshold_kernel(StreamArgs a) 
   if (threadIdx.x == 0) a.thr[t] = thr;
 }
 
-constexpr int kFinNT = 256;                              // finalize
+constexpr int kFinNT = 512;                              // finalize
+constexpr int kFinPer = 7168 / kFinNT;                   // register-held candidates per thread
+constexpr int kFinLoad = 8;                              // staged entries per thread and batch
 constexpr int kRedoNT = 512;                             // fallback
 constexpr int kRedoBatch = kRedoNT * 4 * kUnr;           // tokens per recomputed batch (fallback)
 // LDS layout of the batch buffer on the candidate path: keys [cap], tokens
@@ -207,7 +209,10 @@ __global__ void __launch_bounds__(kFinNT) stream_finalize_kernel(StreamArgs a) {
   __shared__ uint32_t tmp[kUnr * kFinNT / 64];
   __shared__ BinSel res;
   __shared__ __attribute__((aligned(16))) char big[kFinSegOff + 16 * kStreamMaxSegs];
-  static_assert(kStreamMaxSegs == 2 * kFinNT, "two segments per thread in the offset scan");
+  static_assert(kStreamMaxSegs <= 2 * kFinNT, "at most two segments per thread in the offset scan");
+  static_assert(kUnr * kFinNT / 64 >= 4 * kFinNT / 64, "room for the range words after the scan words");
+  static_assert(kFinPer * kFinNT >= 7168 && kFinPer <= 32, "every candidate held in registers");
+  static_assert(4 * kStreamMaxSegs * 4 >= kBins1 * 4, "the second histogram fits the segment tables");
 
   const int t = blockIdx.x;
   int b, pos;
@@ -256,36 +261,94 @@ __global__ void __launch_bounds__(kFinNT) stream_finalize_kernel(StreamArgs a) {
   if (j0 < nseg) soff[j0] = ex;
   if (j0 + 1 < nseg) soff[j0 + 1] = ex + c0;
   lds_barrier();
-  // stage the segments in token order: 32 threads per segment, 4 loads in
-  // flight each; every pair also counts its top key bits (the first radix pass)
+  // stage the segments in token order: tpc threads (a power of two) per
+  // segment, kFinLoad entries per thread and batch, every load of a batch
+  // issued before any is stored, so a batch costs one memory latency; each
+  // thread keeps the smallest and largest key it staged
   const uint2* lists = a.lists + (int64_t)t * a.cap;
-  const int l32 = threadIdx.x & 31;
-  for (uint32_t sl = threadIdx.x >> 5; sl < nseg; sl += kFinNT / 32) {
-    const uint32_t inf = sinfo[sorder[sl]];
-    const uint32_t base = inf >> 16, cnt = inf & 0xFFFFu, o = soff[sl];
-    for (uint32_t e0 = 0; e0 < cnt; e0 += 4 * 32) {
-      uint2 v[4];
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  {
+    int tpc = kFinNT;
+    while (tpc > 1 && tpc * (int)nseg > kFinNT) tpc >>= 1;
+    const int l = threadIdx.x & (tpc - 1);
+    uint32_t lo = 0xFFFFFFFFu, hi = 0u;
+    for (uint32_t sl = threadIdx.x / tpc; sl < nseg; sl += kFinNT / tpc) {
+      const uint32_t inf = sinfo[sorder[sl]];
+      const uint32_t base = inf >> 16, cnt = inf & 0xFFFFu, o = soff[sl];
+      for (uint32_t e0 = 0; e0 < cnt; e0 += (uint32_t)(kFinLoad * tpc)) {
+        uint2 v[kFinLoad];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const uint32_t e = e0 + u * 32 + l32;
-        v[u] = e < cnt ? lists[base + e] : make_uint2(0u, 0u);
-      }
+        for (int u = 0; u < kFinLoad; ++u) {
+          const uint32_t e = e0 + (uint32_t)(l + u * tpc);
+          v[u] = e < cnt ? lists[base + e] : make_uint2(0u, 0u);
+        }
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const uint32_t e = e0 + u * 32 + l32;
-        if (e < cnt) {
-          lkey[o + e] = v[u].x;
-          lidx[o + e] = (int)v[u].y;
-          atomicAdd(&hist[v[u].x >> (32 - kBins1Bits)], 1u);
+        for (int u = 0; u < kFinLoad; ++u) {
+          const uint32_t e = e0 + (uint32_t)(l + u * tpc);
+          if (e < cnt) {
+            lkey[o + e] = v[u].x;
+            lidx[o + e] = (int)v[u].y;
+            lo = min(lo, v[u].x);
+            hi = max(hi, v[u].x);
+          }
         }
       }
     }
+    lo = wave_min_u32(lo);
+    hi = wave_max_u32(hi);
+    // (tmp[2NW..4NW): the compaction scan below writes tmp[0..NW) with no
+    // barrier in between when no radix pass runs)
+    if (lane == 0) {
+      tmp[2 * kFinNT / 64 + wid] = lo;
+      tmp[3 * kFinNT / 64 + wid] = hi;
+    }
   }
-  lds_barrier();
-  const BinSel s1 = select_bin<kFinNT>(hist, kBins1, k, tmp, &res);
-  const LdsSrc ls{lkey, lidx, (int)total};
-  refine_and_emit<kFinNT>(ls, s1.bin, kBins1Bits, k - s1.above, s1.cnt, hist, tmp, &res, k,
-                          [&](uint32_t slot, uint32_t, int id) { out[slot] = id; });
+  lds_barrier();                                   // candidates staged, ranges in; the segment tables are free
+  uint32_t lo = 0xFFFFFFFFu, hi = 0u;
+#pragma unroll
+  for (int w = 0; w < kFinNT / 64; ++w) {
+    lo = min(lo, tmp[2 * kFinNT / 64 + w]);
+    hi = max(hi, tmp[3 * kFinNT / 64 + w]);
+  }
+  // thread-owned consecutive candidates, ranked as key - lo: the radix
+  // passes start at the highest bit that key - lo can have set, which spreads
+  // the candidates (all from the row's upper tail) over the bins
+  const int i0 = threadIdx.x * kFinPer;
+  const int nv = max(0, min(kFinPer, (int)total - i0));
+  uint32_t key[kFinPer];
+  int id[kFinPer];
+#pragma unroll
+  for (int j = 0; j < kFinPer; ++j) {
+    key[j] = j < nv ? lkey[i0 + j] - lo : 0u;
+    id[j] = j < nv ? lidx[i0 + j] : -1;
+  }
+  uint32_t P = 0, need = k, cb = total;
+  int pbits = hi > lo ? __clz(hi - lo) : 32;
+  const uint32_t vm = nv >= 32 ? 0xFFFFFFFFu : (1u << nv) - 1u;
+  // hist (cleared before the staging) and the segment tables' space alternate
+  reg_radix<kFinNT, kFinPer>(key, vm, hist, reinterpret_cast<uint32_t*>(big + kFinSegOff), &res, P, pbits, need, cb);
+  // ordered compaction: every candidate above prefix P, and the first `need`
+  // at it (the smallest tokens among equal keys)
+  uint32_t gm = 0u, em = 0u;
+#pragma unroll
+  for (int j = 0; j < kFinPer; ++j) {
+    const uint32_t pre = key_prefix(key[j], pbits);
+    gm |= (j < nv && pre > P ? 1u : 0u) << j;
+    em |= (j < nv && pre == P ? 1u : 0u) << j;
+  }
+  uint32_t tot2;
+  const uint32_t ex2 = block_exclusive_scan<kFinNT>((uint32_t)__popc(gm) | ((uint32_t)__popc(em) << 16), tmp, tot2);
+  uint32_t gr = ex2 & 0xFFFFu, er = ex2 >> 16;
+#pragma unroll
+  for (int j = 0; j < kFinPer; ++j) {
+    if ((gm >> j) & 1u) {
+      out[gr + min(er, need)] = id[j];
+      ++gr;
+    } else if ((em >> j) & 1u) {
+      if (er < need) out[gr + er] = id[j];
+      ++er;
+    }
+  }
 }
 
 // Rows the finalize could not select from their candidates: each is redone by

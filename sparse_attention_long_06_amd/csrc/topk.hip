@@ -281,116 +281,6 @@ __global__ void __launch_bounds__(kFinalNT) topk_finalize_kernel(TopkArgs a) {
 // candidates (all from the upper tail of the row) over the histogram bins
 // instead of piling them into the few bins their top 11 bits share.
 
-// Selection steps shared by the two launches.  Elements stay in registers:
-// a thread owns PER consecutive elements, so source order is (thread, slot)
-// order and an ordered compaction needs one block scan.  The boundary bin of
-// a histogram is found by wave 0 alone while the other waves clear the
-// histogram of the next pass (two alternate), so a pass costs two barriers.
-
-// Top `pbits` bits of a key (0 when pbits is 0).
-__device__ __forceinline__ uint32_t key_prefix(uint32_t key, int pbits) {
-  return pbits == 0 ? 0u : key >> (32 - pbits);
-}
-
-// Wave-wide min / max with DPP row shifts and row broadcasts (the pattern of
-// wave_inclusive_scan; lanes with no source read the identity), then lane 63.
-__device__ __forceinline__ uint32_t wave_min_u32(uint32_t x) {
-  constexpr int kId = -1;                          // 0xFFFFFFFF
-  x = min(x, (uint32_t)__builtin_amdgcn_update_dpp(kId, (int)x, 0x111, 0xf, 0xf, false));
-  x = min(x, (uint32_t)__builtin_amdgcn_update_dpp(kId, (int)x, 0x112, 0xf, 0xf, false));
-  x = min(x, (uint32_t)__builtin_amdgcn_update_dpp(kId, (int)x, 0x114, 0xf, 0xf, false));
-  x = min(x, (uint32_t)__builtin_amdgcn_update_dpp(kId, (int)x, 0x118, 0xf, 0xf, false));
-  x = min(x, (uint32_t)__builtin_amdgcn_update_dpp(kId, (int)x, 0x142, 0xa, 0xf, false));
-  x = min(x, (uint32_t)__builtin_amdgcn_update_dpp(kId, (int)x, 0x143, 0xc, 0xf, false));
-  return (uint32_t)__builtin_amdgcn_readlane((int)x, 63);
-}
-
-__device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
-  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xf, 0xf, false));
-  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xf, 0xf, false));
-  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xf, 0xf, false));
-  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xf, 0xf, false));
-  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x142, 0xa, 0xf, false));
-  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x143, 0xc, 0xf, false));
-  return (uint32_t)__builtin_amdgcn_readlane((int)x, 63);
-}
-
-// Wave 0 only: the bin of hist[0, nb) (nb <= kBins1, a power of two),
-// scanning from the top, where the running count reaches `need`, the count
-// above it and its own count, written to *res.  Two wave scans: lane l sums
-// the `per` bins at descending positions per*l .. per*l + per - 1 (bin
-// nb - 1 - position); then lanes 0 .. per-1 scan the bins of the lane whose
-// range holds the boundary.
-__device__ __forceinline__ void wave_select_bin(const uint32_t* hist, int nb, uint32_t need, BinSel* res) {
-  static_assert(kBins1 == 64 * 32, "at most 32 bins per lane");
-  const int lane = threadIdx.x & 63;
-  const int per = nb >= 64 ? nb >> 6 : 1;
-  uint32_t c = 0;
-  if (per == 32) {
-    const uint4* p = reinterpret_cast<const uint4*>(hist + nb - 32 * (lane + 1));
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const uint4 x = p[q];
-      c += x.x + x.y + x.z + x.w;
-    }
-  } else {
-    for (int j = 0; j < per; ++j) {
-      const int d = lane * per + j;
-      if (d < nb) c += hist[nb - 1 - d];
-    }
-  }
-  const uint32_t incl = wave_inclusive_scan(c);
-  const unsigned long long hit = __ballot(incl - c < need && need <= incl);
-  if (hit == 0ull) return;                         // need exceeds the histogram's total (callers never ask)
-  const int L = __builtin_ctzll(hit);
-  const uint32_t run0 = (uint32_t)__shfl((int)(incl - c), L);
-  const int d = L * per + lane;
-  const uint32_t v = (lane < per && d < nb) ? hist[nb - 1 - d] : 0u;
-  const uint32_t incl2 = wave_inclusive_scan(v) + run0;
-  if (lane < per && incl2 - v < need && need <= incl2) {
-    res->bin = (uint32_t)(nb - 1 - d);
-    res->above = incl2 - v;
-    res->cnt = v;
-  }
-}
-
-// Radix passes over register-held keys (PER per thread, bit j of vm set for
-// the valid ones) until the boundary prefix is exact or needed whole, or
-// pbits reaches max_pbits.  hist[0] and hist[1] must be clear on entry; P /
-// pbits / need / cnt carry the state in and out (cnt: keys sharing the
-// current prefix; need: how many of them the selection takes, <= cnt).
-template <int NT, int PER>
-__device__ __forceinline__ void reg_radix(const uint32_t (&key)[PER], uint32_t vm, uint32_t (*hist)[kBins1],
-                                          BinSel* res, uint32_t& P, int& pbits, uint32_t& need, uint32_t& cnt,
-                                          int max_pbits = 32) {
-  static_assert(PER <= 32, "32-bit validity mask");
-  const int wid = threadIdx.x >> 6;
-  int cur = 0;
-  while (cnt != need && pbits < max_pbits) {       // uniform
-    const int bits = 32 - pbits < kBins1Bits ? 32 - pbits : kBins1Bits;
-    const int shift = 32 - pbits - bits;
-    const uint32_t mask = (1u << bits) - 1u;
-    uint32_t* hc = hist[cur];
-#pragma unroll
-    for (int j = 0; j < PER; ++j)
-      if (((vm >> j) & 1u) && key_prefix(key[j], pbits) == P) atomicAdd(&hc[(key[j] >> shift) & mask], 1u);
-    lds_barrier();                                 // the histogram is complete
-    if (wid == 0) {
-      wave_select_bin(hc, 1 << bits, need, res);
-    } else {
-      uint32_t* hn = hist[cur ^ 1];
-      for (int i = threadIdx.x - 64; i < kBins1; i += NT - 64) hn[i] = 0u;
-    }
-    lds_barrier();                                 // *res is set, the next histogram clear
-    const BinSel s = *res;
-    P = (P << bits) | s.bin;
-    pbits += bits;
-    need -= s.above;
-    cnt = s.cnt;
-    cur ^= 1;
-  }
-}
-
 // ---- launch 1: per-chunk candidates
 
 constexpr int kChunkNT = 512;
@@ -449,7 +339,7 @@ __global__ void __launch_bounds__(kChunkNT) topk_chunk_kernel(CandArgs a) {
     for (int i = threadIdx.x; i < 2 * kBins1; i += kChunkNT) (&hist[0][0])[i] = 0u;
     lds_barrier();
     uint32_t need = C, cnt = (uint32_t)nk;
-    reg_radix<kChunkNT, kChunkPer>(key, vm, hist, &res, P, pbits, need, cnt, 2 * kBins1Bits);
+    reg_radix<kChunkNT, kChunkPer>(key, vm, hist[0], hist[1], &res, P, pbits, need, cnt, 2 * kBins1Bits);
   }
   uint32_t keep = 0u;
 #pragma unroll
@@ -655,7 +545,7 @@ __global__ void __launch_bounds__(kCandNT) topk_cand_kernel(CandArgs a) {
     uint32_t P = 0, need = k, cb = m;
     int pbits = hi > lo ? __clz(hi - lo) : 32;
     const uint32_t vm = nv >= 32 ? 0xFFFFFFFFu : (1u << nv) - 1u;
-    reg_radix<kCandNT, kCandPer>(key, vm, hist, &res, P, pbits, need, cb);
+    reg_radix<kCandNT, kCandPer>(key, vm, hist[0], hist[1], &res, P, pbits, need, cb);
     // ordered compaction: every key above prefix P, and the first `need` at it
     uint32_t gm = 0u, em = 0u;
 #pragma unroll
