@@ -40,6 +40,10 @@ namespace dsa {
 
 constexpr int kRowNT = 512;
 constexpr int kRowCap = 8192;
+constexpr int kRowPer = kRowCap / kRowNT;          // register-held candidates per thread
+constexpr int kRowUnr = 4;                         // load batches of the passes over a row's scores
+static_assert(kRowPer <= 32 && kUnr * kRowNT / 64 >= 4 * kRowNT / 64, "candidate mask; range words after the scan words");
+static_assert(kRowCap >= kBins1, "the key array holds the second histogram");
 
 __global__ void __launch_bounds__(kRowNT) topk_row_kernel(TopkArgs a) {
   __shared__ uint32_t hist[kBins1];
@@ -61,22 +65,84 @@ __global__ void __launch_bounds__(kRowNT) topk_row_kernel(TopkArgs a) {
   const RowSrc row{a.scores + (int64_t)t * a.ld, n, 0};
   auto to_out = [&](uint32_t slot, uint32_t, int id) { out[slot] = id; };
 
-  hist_pass<kRowNT>(row, hist, 0u, 0, 32 - kBins1Bits, kBins1Bits);
+  hist_pass<kRowNT, kRowUnr>(row, hist, 0u, 0, 32 - kBins1Bits, kBins1Bits);
   const BinSel s1 = select_bin<kRowNT>(hist, kBins1, k, tmp, &res);
   const uint32_t need = k - s1.above;
   if (s1.cnt == need) {
-    compact<kRowNT>(row, s1.bin, kBins1Bits, need, k, tmp, to_out);
+    compact<kRowNT, kRowUnr>(row, s1.bin, kBins1Bits, need, k, tmp, to_out);
     return;
   }
   const uint32_t m = s1.above + s1.cnt;
   if (m <= (uint32_t)kRowCap) {
-    compact<kRowNT>(row, s1.bin, kBins1Bits, s1.cnt, m, tmp,
+    // the m keys at or above the boundary bin, in token order, into LDS; then
+    // into registers (kRowPer consecutive ones per thread) as offsets from
+    // their smallest, for the register radix passes and one ordered
+    // compaction.  The first pass's histogram (cleared here) and the key
+    // array (free once the keys are in registers) are the two histograms.
+    compact<kRowNT, kRowUnr>(row, s1.bin, kBins1Bits, s1.cnt, m, tmp,
                     [&](uint32_t slot, uint32_t key, int id) { lkey[slot] = key; lidx[slot] = id; });
+    for (int i = threadIdx.x; i < kBins1; i += kRowNT) hist[i] = 0u;
     lds_barrier();
-    const LdsSrc ls{lkey, lidx, (int)m};
-    refine_and_emit<kRowNT>(ls, s1.bin, kBins1Bits, need, s1.cnt, hist, tmp, &res, k, to_out);
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+    const int i0 = threadIdx.x * kRowPer;
+    const int nv = max(0, min(kRowPer, (int)m - i0));
+    uint32_t key[kRowPer];
+    int id[kRowPer];
+    uint32_t lo = 0xFFFFFFFFu, hi = 0u;
+#pragma unroll
+    for (int j = 0; j < kRowPer; ++j) {
+      key[j] = j < nv ? lkey[i0 + j] : 0u;
+      id[j] = j < nv ? lidx[i0 + j] : -1;
+      if (j < nv) {
+        lo = min(lo, key[j]);
+        hi = max(hi, key[j]);
+      }
+    }
+    lo = wave_min_u32(lo);
+    hi = wave_max_u32(hi);
+    // (tmp[2NW..4NW): the compaction scan below writes tmp[0..NW) with no
+    // barrier in between when no radix pass runs)
+    if (lane == 0) {
+      tmp[2 * kRowNT / 64 + wid] = lo;
+      tmp[3 * kRowNT / 64 + wid] = hi;
+    }
+    lds_barrier();                                 // keys in registers (LDS keys free), ranges in
+    lo = 0xFFFFFFFFu;
+    hi = 0u;
+#pragma unroll
+    for (int w = 0; w < kRowNT / 64; ++w) {
+      lo = min(lo, tmp[2 * kRowNT / 64 + w]);
+      hi = max(hi, tmp[3 * kRowNT / 64 + w]);
+    }
+#pragma unroll
+    for (int j = 0; j < kRowPer; ++j) key[j] -= lo;
+    uint32_t P = 0, need2 = k, cb = m;
+    int pbits = hi > lo ? __clz(hi - lo) : 32;
+    const uint32_t vm = nv >= 32 ? 0xFFFFFFFFu : (1u << nv) - 1u;
+    reg_radix<kRowNT, kRowPer>(key, vm, hist, lkey, &res, P, pbits, need2, cb);
+    // ordered compaction: every key above prefix P, and the first need2 at it
+    uint32_t gm = 0u, em = 0u;
+#pragma unroll
+    for (int j = 0; j < kRowPer; ++j) {
+      const uint32_t pre = key_prefix(key[j], pbits);
+      gm |= (j < nv && pre > P ? 1u : 0u) << j;
+      em |= (j < nv && pre == P ? 1u : 0u) << j;
+    }
+    uint32_t tot2;
+    const uint32_t ex = block_exclusive_scan<kRowNT>((uint32_t)__popc(gm) | ((uint32_t)__popc(em) << 16), tmp, tot2);
+    uint32_t gr = ex & 0xFFFFu, er = ex >> 16;
+#pragma unroll
+    for (int j = 0; j < kRowPer; ++j) {
+      if ((gm >> j) & 1u) {
+        out[gr + min(er, need2)] = id[j];
+        ++gr;
+      } else if ((em >> j) & 1u) {
+        if (er < need2) out[gr + er] = id[j];
+        ++er;
+      }
+    }
   } else {
-    refine_and_emit<kRowNT>(row, s1.bin, kBins1Bits, need, s1.cnt, hist, tmp, &res, k, to_out);
+    refine_and_emit<kRowNT, kRowUnr>(row, s1.bin, kBins1Bits, need, s1.cnt, hist, tmp, &res, k, to_out);
   }
 }
 
