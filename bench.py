@@ -804,9 +804,10 @@ def main():
 
 
 def other_workloads(args, att=None):
-    """The mixed-length paged decode and the 32K streaming prefill, timed in the
-    same run as the headline (their own roofline fractions beside it; `att`:
-    the headline's attainable-peak measurements, if taken)."""
+    """The mixed-length paged decode and the 32K prefill (streaming selection,
+    then the staged entry points), timed in the same run as the headline
+    (their own roofline fractions beside it; `att`: the headline's
+    attainable-peak measurements, if taken)."""
     out = {}
     print("[bench] paged_decode_b128_mixed4k_128k", file=sys.stderr, flush=True)
     r, _ = run_bench(args, workload="paged_decode_b128_mixed4k_128k", separate_calls=False, attainable=False)
@@ -832,6 +833,14 @@ def other_workloads(args, att=None):
             p["indexer"]["TFLOP/s"] / att["mfma_16x16x32_bf16_TFLOP/s"], 4)
         out["prefill_L32k"]["attention"]["attainable_bf16_frac"] = round(
             p["attention"]["TFLOP/s"] / att["mfma_32x32x16_bf16_TFLOP/s"], 4)
+    # the same pass through the three staged entry points (score matrix in HBM)
+    print("[bench] prefill_L32k (staged selection)", file=sys.stderr, flush=True)
+    del p
+    sargs = argparse.Namespace(**vars(pargs))
+    sargs.select = "staged"
+    q = run_prefill(sargs, attainable=False)
+    out["prefill_L32k_staged"] = {k: q[k] for k in ("metric", "value", "unit", "ms_per_step", "steps", "stages_ms",
+                                                    "memory")}
     return out
 
 
