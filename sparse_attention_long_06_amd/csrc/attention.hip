@@ -443,20 +443,52 @@ attn_wide_kernel(AttnArgs a) {
     dma_rows(tile % kWideSlots, a.kv.data, a.kv.row_stride, row, wave);
   };
 
-  // Prologue.  Vector-memory loads complete in order, so a load queued behind
-  // the 147 KB q DMA would wait for all of it: the row's sequence and
-  // position are read first, then the split's selected token ids (and, for
-  // paged caches, their block ids) come into rowid[] by LDS DMA ahead of q,
-  // and the token rows are formed from LDS while q is in flight.
+  // Prologue.  This wave's q block (heads h0..h0+31: 36,864 contiguous
+  // bytes, ring slot `wave`) needs only the row, so its DMA goes first; the
+  // row's sequence and position are read meanwhile, then the split's selected
+  // token ids (and, for paged caches, their block ids) come into rowid[] by
+  // LDS DMA.  Vector-memory loads complete in order, so the ids are in once
+  // everything is, and no compiler-visible load sits behind the DMA.
+  {
+    const char* qblock = reinterpret_cast<const char*>(a.q + ((int64_t)t * a.H + h0) * D);
+#pragma unroll
+    for (int part = 0; part < kWideWaves; ++part)
+      dma_rows(wave, qblock, (int64_t)D * 2, (uint32_t)(8 * part + drow), part);
+  }
+  // The row's sequence and position (as row_seq_pos) through the scalar
+  // cache: the tables are read-only here, and scalar loads do not queue
+  // behind the DMA on the vector-memory counter.
   int b, pos;
-  row_seq_pos(a.g, t, b, pos);
+  {
+    typedef const __attribute__((address_space(4))) int32_t cint;
+    cint* lens = (cint*)(uintptr_t)a.g.seq_lens;
+    if (!a.g.q_start) {
+      b = t;
+      pos = lens[t] - 1;
+    } else {
+      cint* qst = (cint*)(uintptr_t)a.g.q_start;
+      int lo = 0, hi = a.g.num_seqs - 1;            // largest b with q_start[b] <= t
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (qst[mid] <= t) lo = mid; else hi = mid - 1;
+      }
+      b = lo;
+      pos = lens[b] - (qst[b + 1] - qst[b]) + (t - qst[b]);
+    }
+  }
   const int slot_beg = split * a.per_split;
   const int nslots = min(a.k, slot_beg + a.per_split) - slot_beg;
   const int ntiles = (nslots + kWideRows - 1) / kWideRows;
   const int32_t* sel = a.idx + (int64_t)t * a.k + slot_beg;
   // invalid slots borrow token 0 of the sequence (finite values, zero weight)
-  const uint32_t fallback = (uint32_t)token_row(a.g, a.kv, b, 0);
-  asm volatile("" :: "v"(fallback), "v"(pos));    // those loads are complete before any DMA is queued
+  uint32_t fallback;
+  if (a.g.block_table) {
+    typedef const __attribute__((address_space(4))) int32_t cint;
+    const int blk = ((cint*)(uintptr_t)a.g.block_table)[(int64_t)b * a.g.max_blocks];
+    fallback = (uint32_t)((int64_t)blk << a.g.block_shift);
+  } else {
+    fallback = (uint32_t)((int64_t)b * a.kv.seq_stride);
+  }
   const uint32_t rid_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)&rowid[0];
   // 4-byte LDS DMA of this lane's word for slot i = 256 m + 64 wave + lane into rowid[i]
   auto dma_slot = [&](int m, const void* src) {
@@ -470,7 +502,7 @@ attn_wide_kernel(AttnArgs a) {
   }
   int sv[SPT];          // paged: the slots' token ids, kept while their block ids arrive
   if (a.g.block_table) {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");      // only the id DMA is outstanding
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");      // the id words (and q) are in
 #pragma unroll
     for (int m = 0; m < SPT; ++m) {
       const int i = threadIdx.x + m * 64 * kWideWaves;
@@ -480,17 +512,10 @@ attn_wide_kernel(AttnArgs a) {
       if (sm >= 0) dma_slot(m, a.g.block_table + (int64_t)b * a.g.max_blocks + (sm >> a.g.block_shift));
     }
   }
-  // this wave's q block (heads h0..h0+31: 36,864 contiguous bytes) into slot `wave`
-  {
-    const char* qblock = reinterpret_cast<const char*>(a.q + ((int64_t)t * a.H + h0) * D);
-#pragma unroll
-    for (int part = 0; part < kWideWaves; ++part)
-      dma_rows(wave, qblock, (int64_t)D * 2, (uint32_t)(8 * part + drow), part);
-  }
-  // at most the 36 q instructions outstanding: this lane's id (block id)
-  // words are in LDS.  Each slot's word was fetched by the lane that now
-  // reads and replaces it with the token row; one validity bit per slot.
-  asm volatile("s_waitcnt vmcnt(%0)" :: "n"(kWideWaves * NIW) : "memory");
+  // q and this lane's id (block id) words are in LDS.  Each slot's word was
+  // fetched by the lane that now reads and replaces it with the token row;
+  // one validity bit per slot.
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 #pragma unroll
   for (int m = 0; m < SPT; ++m) {
     const int i = threadIdx.x + m * 64 * kWideWaves;
