@@ -337,17 +337,20 @@ __global__ void __launch_bounds__(512) attn_kernel(AttnArgs a) {
 // 256 registers) stay in the wave's 512-entry register file for the whole
 // split, so every K or V element read from LDS feeds 32 heads (twice the
 // reuse of 16-head waves, half the LDS traffic per FLOP).
-//   * tiles of 32 selected rows, gathered by LDS DMA into a 4-slot ring
-//     (three tiles in flight while one is computed).  Before the first tile
-//     each wave stages its q block (32 heads x 576 dims, contiguous in HBM)
-//     through slot w the same way, with 1 KB coalesced DMA instructions, and
-//     reads its fragments from there: loading them straight into registers
-//     touches 32 rows per instruction and took several microseconds;
+//   * tiles of 32 selected rows, gathered by LDS DMA into a 4-slot ring: an
+//     iteration reads two tiles (V of tile j, K of tile j+1) while two more
+//     are in flight.  Before the first tile each wave stages its q block (32
+//     heads x 576 dims, contiguous in HBM) through slot w the same way, with
+//     1 KB coalesced DMA instructions, and reads its fragments from there:
+//     loading them straight into registers touches 32 rows per instruction
+//     and took several microseconds.  The q DMA is issued first; the row's
+//     sequence metadata is read by scalar loads meanwhile and the selected
+//     ids follow by 4-byte LDS DMA;
 //   * S^T = K q^T: A = 32 rows x 16 dims of K (one ds_read_b128 per lane), B =
 //     q (registers).  Lane l ends with head l%32 and rows 8(i/4)+4(l/32)+i%4
 //     in accumulator i, so a head's softmax is 16 in-lane values and one
 //     exchange with lane l^32;
-//   * O^T += V^T P^T: A = V^T read transposed from the row-major tile with
+//   * O^T += V^T P^T: A = V^T read transposed from the tile with
 //     ds_read_b64_tr_b16 (a 16-lane group reads 4 rows x 16 dims and lane i
 //     receives the 4 rows of dim i; two reads give a lane the 8 rows of its
 //     K slots), B = P^T straight from the S^T accumulators (K slot j of
@@ -355,6 +358,9 @@ __global__ void __launch_bounds__(512) attn_kernel(AttnArgs a) {
 //     operands).  Lane l then holds dims 8(i/4) + 4(l/32) + i%4 of every
 //     32-dim tile of head l%32 only: a head's rescale and final 1/l are the
 //     lane's own factors, with no exchange;
+//   * software pipeline: the softmax of tile j (masking, max, exponentials,
+//     bf16 rounding) runs on the VALU between the 36 matrix-core steps of
+//     tile j+1's S^T, then P V of tile j follows;
 //   * a tile is stored in nine blocks of 8 chunks (128 bytes of each row):
 //     16-byte chunk c of row r sits at byte 4096 (c/8) + 128 r +
 //     16 ((c%8) ^ f(r)), f(r) = ((r>>1 & 1) << 2) | (r>>2 & 3), so the 16
@@ -365,7 +371,7 @@ __global__ void __launch_bounds__(512) attn_kernel(AttnArgs a) {
 //     row-id read and one 64-bit address per lane, the block as an immediate
 //     offset.
 constexpr int kWideRows = 32;       // selected rows per tile
-constexpr int kWideSlots = 4;       // tiles in the LDS ring (three in flight while one is computed)
+constexpr int kWideSlots = 4;       // tiles in the LDS ring (two read, two in flight)
 constexpr int kWideWaves = 4;       // 32 heads each
 
 typedef float v16f __attribute__((ext_vector_type(16)));
