@@ -834,6 +834,70 @@ __global__ void __launch_bounds__(256) attn_combine_kernel(CombineArgs a) {
   if (a.lse && d8 == 0) a.lse[th] = lse;
 }
 
+// The same merge for NS = 2 or 4 splits: a thread merges 8 / NS items (256
+// apart, so each of its passes is one coalesced sweep) and issues the loads of
+// all of them before it uses any, which keeps eight 16-byte partial loads in
+// flight per thread as the general kernel does at eight splits.  The
+// arithmetic per item is the general kernel's, in the same order.
+template <int NS>
+__global__ void __launch_bounds__(256) attn_combine_few_kernel(CombineArgs a) {
+  constexpr int IPT = 8 / NS;
+  const int per_head = a.D_v / 8;
+  const int64_t total = (int64_t)a.T * a.H * per_head;
+  const int64_t base = (int64_t)xcd_major(blockIdx.x, gridDim.x) * (256 * IPT) + threadIdx.x;
+  const int64_t po_stride = (int64_t)a.H * a.D_v;
+  float wl[IPT][NS];
+  v4i raw[IPT][NS];
+#pragma unroll
+  for (int i = 0; i < IPT; ++i) {
+    const int64_t item = base + 256 * i;
+    const bool ok = item < total;
+    const int64_t it = ok ? item : 0;
+    const int d8 = (int)(it % per_head);
+    const int64_t th = it / per_head;          // t * H + h
+    const int h = (int)(th % a.H);
+    const int t = (int)(th / a.H);
+    const float* pl = a.part_lse + (int64_t)t * NS * a.H + h;
+    const uint16_t* po = a.part_o + ((int64_t)t * NS * a.H + h) * a.D_v + d8 * 8;
+#pragma unroll
+    for (int j = 0; j < NS; ++j) {
+      wl[i][j] = ok ? pl[(int64_t)j * a.H] : -INFINITY;
+      raw[i][j] = ok ? *reinterpret_cast<const v4i*>(po + j * po_stride) : v4i{0, 0, 0, 0};
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < IPT; ++i) {
+    const int64_t item = base + 256 * i;
+    if (item >= total) break;
+    float mx = -INFINITY, den = 0.0f;
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < NS; ++j) mx = fmaxf(mx, wl[i][j]);
+    float lse = -INFINITY;
+    if (mx != -INFINITY) {
+#pragma unroll
+      for (int j = 0; j < NS; ++j) {
+        const float wgt = __expf(wl[i][j] - mx);
+        den += wgt;
+        const v8bf pv = __builtin_bit_cast(v8bf, raw[i][j]);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] += wgt * (float)pv[e];
+      }
+      lse = mx + __logf(den);
+      const float inv = 1.0f / den;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] *= inv;
+    }
+    uint32_t pk[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) pk[j] = (uint32_t)bf16_bits(acc[2 * j]) | ((uint32_t)bf16_bits(acc[2 * j + 1]) << 16);
+    const int d8 = (int)(item % per_head);
+    const int64_t th = item / per_head;
+    *reinterpret_cast<v4i*>(a.out + th * a.D_v + d8 * 8) = v4i{(int)pk[0], (int)pk[1], (int)pk[2], (int)pk[3]};
+    if (a.lse && d8 == 0) a.lse[th] = lse;
+  }
+}
+
 hipError_t launch_attn(const AttnArgs& a, int D, int D_v, hipStream_t stream) {
   const dim3 grid((unsigned)((int64_t)a.g.num_rows * a.nsplit));
   const bool sepv = a.v.data != nullptr;
@@ -854,7 +918,13 @@ hipError_t launch_attn(const AttnArgs& a, int D, int D_v, hipStream_t stream) {
 
 hipError_t launch_combine(const CombineArgs& a, hipStream_t stream) {
   const int64_t items = (int64_t)a.T * a.H * (a.D_v / 8);
-  hipLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)((items + 255) / 256)), dim3(256), 0, stream, a);
+  if (a.nsplit == 2) {
+    hipLaunchKernelGGL(attn_combine_few_kernel<2>, dim3((unsigned)((items + 1023) / 1024)), dim3(256), 0, stream, a);
+  } else if (a.nsplit == 4) {
+    hipLaunchKernelGGL(attn_combine_few_kernel<4>, dim3((unsigned)((items + 511) / 512)), dim3(256), 0, stream, a);
+  } else {
+    hipLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)((items + 255) / 256)), dim3(256), 0, stream, a);
+  }
   return hipGetLastError();
 }
 

@@ -171,7 +171,8 @@ def test_attention_ragged_and_padded_index_sets():
 
 def test_attention_split_counts_agree():
     """The split-K form of the online softmax: one decode input attended with 1,
-    2 and 8 splits per row (dsa_set_attn_splits).  Each split writes its
+    2, 4 and 8 splits per row (dsa_set_attn_splits; 2 and 4 splits take the
+    merge kernel that handles several items per thread).  Each split writes its
     normalised partial output in bf16 (relative rounding 2^-9) and its lse in
     fp32; the merge weights sum to one, so two split counts differ by at most
     two bf16 roundings of the partials plus one of the output: |a - b| <=
@@ -186,7 +187,7 @@ def test_attention_split_counts_agree():
     idx = dsa.topk(batch, scores, wl.k)
     res = {}
     try:
-        for ns in (1, 2, 8):
+        for ns in (1, 2, 4, 8):
             dsa.set_attn_splits(ns)
             runs = [dsa.sparse_attn(batch, inp.q, inp.kv, inp.v, wl.scale, idx, D_v=wl.D_v) for _ in range(2)]
             torch.cuda.synchronize()
@@ -197,7 +198,7 @@ def test_attention_split_counts_agree():
         dsa.set_attn_splits(0)
     o1, l1 = res[1]
     scale = np.abs(o1).max()
-    for ns in (2, 8):
+    for ns in (2, 4, 8):
         o, l = res[ns]
         assert np.abs(o - o1).max() <= 4 * 2.0 ** -7 * scale, f"nsplit {ns}: {np.abs(o - o1).max()} vs {scale}"
         assert np.allclose(l, l1, rtol=0, atol=1e-5), f"nsplit {ns}: lse off {np.abs(l - l1).max()}"
