@@ -317,10 +317,17 @@ __global__ void __launch_bounds__(kFinNT) stream_finalize_kernel(StreamArgs a) {
   const int nv = max(0, min(kFinPer, (int)total - i0));
   uint32_t key[kFinPer];
   int id[kFinPer];
+  // every slot read (i0 + kFinPer <= 7168: inside the key and index arrays),
+  // so the reads issue together; slots past the total are masked
 #pragma unroll
   for (int j = 0; j < kFinPer; ++j) {
-    key[j] = j < nv ? lkey[i0 + j] - lo : 0u;
-    id[j] = j < nv ? lidx[i0 + j] : -1;
+    key[j] = lkey[i0 + j];
+    id[j] = lidx[i0 + j];
+  }
+#pragma unroll
+  for (int j = 0; j < kFinPer; ++j) {
+    key[j] = j < nv ? key[j] - lo : 0u;
+    id[j] = j < nv ? id[j] : -1;
   }
   uint32_t P = 0, need = k, cb = total;
   int pbits = hi > lo ? __clz(hi - lo) : 32;

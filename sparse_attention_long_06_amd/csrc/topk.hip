@@ -89,10 +89,17 @@ __global__ void __launch_bounds__(kRowNT) topk_row_kernel(TopkArgs a) {
     uint32_t key[kRowPer];
     int id[kRowPer];
     uint32_t lo = 0xFFFFFFFFu, hi = 0u;
+    // every slot read (i0 + kRowPer <= kRowCap), so the reads issue together
+    // instead of one guarded read after another; slots past m are masked
 #pragma unroll
     for (int j = 0; j < kRowPer; ++j) {
-      key[j] = j < nv ? lkey[i0 + j] : 0u;
-      id[j] = j < nv ? lidx[i0 + j] : -1;
+      key[j] = lkey[i0 + j];
+      id[j] = lidx[i0 + j];
+    }
+#pragma unroll
+    for (int j = 0; j < kRowPer; ++j) {
+      key[j] = j < nv ? key[j] : 0u;
+      id[j] = j < nv ? id[j] : -1;
       if (j < nv) {
         lo = min(lo, key[j]);
         hi = max(hi, key[j]);
@@ -385,9 +392,17 @@ __global__ void __launch_bounds__(kChunkNT) topk_chunk_kernel(CandArgs a) {
       key[4 * j + 2] = score_key(v[j].z);
       key[4 * j + 3] = score_key(v[j].w);
     }
+  } else if (nv > 0) {
+    // the ragged end: every load in bounds (clamped to the last score) and
+    // issued before any is used, instead of one guarded load after another
+    float v[kChunkPer];
+#pragma unroll
+    for (int j = 0; j < kChunkPer; ++j) v[j] = src[i0 + min(j, nv - 1)];
+#pragma unroll
+    for (int j = 0; j < kChunkPer; ++j) key[j] = j < nv ? score_key(v[j]) : 0u;
   } else {
 #pragma unroll
-    for (int j = 0; j < kChunkPer; ++j) key[j] = j < nv ? score_key(src[i0 + j]) : 0u;
+    for (int j = 0; j < kChunkPer; ++j) key[j] = 0u;
   }
 
   uint32_t vm = 0u;
@@ -602,10 +617,16 @@ __global__ void __launch_bounds__(kCandNT) topk_cand_kernel(CandArgs a) {
         id[4 * q] = iv.x; id[4 * q + 1] = iv.y; id[4 * q + 2] = iv.z; id[4 * q + 3] = iv.w;
       }
     } else {
+      // every slot read (i0 + kCandPer <= kCandCap), slots past m masked
 #pragma unroll
       for (int j = 0; j < kCandPer; ++j) {
-        key[j] = j < nv ? lkey[i0 + j] - sub : 0u;
-        id[j] = j < nv ? lidx[i0 + j] : -1;
+        key[j] = lkey[i0 + j];
+        id[j] = lidx[i0 + j];
+      }
+#pragma unroll
+      for (int j = 0; j < kCandPer; ++j) {
+        key[j] = j < nv ? key[j] - sub : 0u;
+        id[j] = j < nv ? id[j] : -1;
       }
     }
     uint32_t P = 0, need = k, cb = m;
