@@ -128,6 +128,67 @@ def test_fp8_filter_equals_exact_filter(wl):
     _oracle_check(inp, idx, out, lse, rows, exact=wl.integer_indexer)
 
 
+def _near_tie_inputs(wl, nclust, seed):
+    """Seeded inputs whose index keys hold a cluster of ``nclust`` near-copies
+    of one key (two dims moved by one e4m3fn code step each, never onto the
+    NaN code) with a key scale four times the largest, so that many rows'
+    sampled thresholds and k-th scores fall inside a dense run of scores that
+    differ by less than the FP8 filter's error margin."""
+    inp = W.generate(wl, "cpu")
+    g = np.random.default_rng(seed)
+    L = inp.seq_lens_host[0]
+    k8 = inp.k8.numpy().copy()
+    ks = inp.k_scale.numpy().copy()
+    base = k8[0, int(g.integers(0, L))].copy()
+    toks = g.choice(L, size=nclust, replace=False)
+    for s in toks:
+        c = base.copy()
+        for d in g.choice(c.shape[0], size=2, replace=False):
+            x = int(c[d]) ^ 1
+            if (x & 0x7F) == 0x7F:
+                x = int(c[d]) - 1
+            c[d] = x
+        k8[0, s] = c
+    ks[0, toks] = ks[0, toks].max() * 4.0
+    inp.k8 = torch.from_numpy(k8)
+    inp.k_scale = torch.from_numpy(ks)
+    return inp.to(DEV)
+
+
+def test_fp8_filter_near_ties_inside_margin():
+    """The FP8 filter where its margin matters: 9000 of 16000 keys are
+    near-copies of one key, so the sampled thresholds and the k-th scores of
+    the thresholded rows sit in runs of hundreds to thousands of scores within
+    1% of each other (checked below on the oracle's scores), and the FP8
+    estimate cannot order them; only the exact rescoring can.  The selection
+    and attention must equal the stored-score path's bit for bit with the
+    filter on and off, and the oracle's on sampled thresholded rows."""
+    wl = W.PREFILL_32K.replace(name="prefill_L16000_near_ties", seq_len=16000, seed=35, sample_rows=0)
+    announce("fp8 filter, near ties inside the margin", wl.name)
+    inp = _near_tie_inputs(wl, 9000, 5)
+    try:
+        dsa.set_indexer_fp8(True)
+        p, s8 = _both(inp)
+    finally:
+        dsa.set_indexer_fp8(False)
+    _assert_same(p, s8, wl.name + " fp8")
+    batch = dsa.Batch.from_inputs(inp)
+    idx_e = torch.empty_like(s8[0])
+    out_e, lse_e, _ = dsa.prefill_streaming(batch, inp.q8, inp.q_scale, inp.w, inp.k8, inp.k_scale, wl.k, inp.q,
+                                            inp.kv, inp.v, wl.scale, idx_out=idx_e, D_v=wl.D_v)
+    torch.cuda.synchronize()
+    _assert_same(p, (idx_e, out_e, lse_e), wl.name + " exact filter")
+    idx, out, lse = (to_np(x) for x in s8)
+    rows = list(range(7200, 16000, 880)) + [inp.num_rows - 1]
+    ref = _oracle_check(inp, idx, out, lse, rows, exact=False)
+    dense = 0
+    for i in range(len(rows)):
+        sc = np.asarray(ref["scores"][i])
+        tau = np.sort(sc)[::-1][wl.k - 1]
+        dense += int(np.count_nonzero(np.abs(sc - tau) <= 0.01 * abs(tau)) >= 100)
+    assert dense >= 3, f"only {dense} checked rows have a dense run of scores at their k-th"
+
+
 def test_streaming_chunked_prefill_late_chunk():
     """A chunk whose rows sit at positions 7500..9999 of a growing cache."""
     wl = W.CHUNKED_128K.replace(name="chunked_prefill_L10000_c2500", seq_len=10000, chunk=2500, seed=35,
