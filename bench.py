@@ -572,9 +572,11 @@ def run_chunked(args, wl):
     }
 
 
-def run_warmup(args):
+def run_warmup(args, att=None):
     """One step = the indexer warm-up objective with all three gradients
-    (dsa_indexer_warmup) over every token of the sequence as a query row."""
+    (dsa_indexer_warmup) over every token of the sequence as a query row.
+    `att`: attainable-peak measurements already taken in this run (measured
+    here when None)."""
     import torch
 
     import workloads as W
@@ -660,13 +662,15 @@ def run_warmup(args):
         "stages_tflops": {k: round(v, 1) for k, v in tfs.items()},
         "wall_s": round(elapsed, 3),
     }
-    att = attainable_peaks()
-    res["attainable"] = att
+    if att is None:
+        att = attainable_peaks()
+        res["attainable"] = att
     # against the fastest measured bf16 matrix-core form (32x32x16); the
     # kernels run the 16x16x32 form, whose own rate gives the second figure
-    best = max(att["mfma_16x16x32_bf16_TFLOP/s"], att["mfma_32x32x16_bf16_TFLOP/s"])
-    res["roofline"]["frac_of_attainable"] = round(tfs[dom] / best, 4)
-    res["roofline"]["frac_of_attainable_form_used"] = round(tfs[dom] / att["mfma_16x16x32_bf16_TFLOP/s"], 4)
+    if att:
+        best = max(att["mfma_16x16x32_bf16_TFLOP/s"], att["mfma_32x32x16_bf16_TFLOP/s"])
+        res["roofline"]["frac_of_attainable"] = round(tfs[dom] / best, 4)
+        res["roofline"]["frac_of_attainable_form_used"] = round(tfs[dom] / att["mfma_16x16x32_bf16_TFLOP/s"], 4)
     if args.no_cpu_baseline:
         res["cpu_baseline"] = None
     else:
@@ -771,7 +775,8 @@ def main():
     ap.add_argument("--workload", default="decode_b32_ctx128k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true",
-                    help="decode headline only: skip the paged-decode and 32K-prefill lines of the default run")
+                    help="decode headline only: skip the paged-decode, prefill, chunked-prefill and warm-up "
+                         "lines of the default run")
     ap.add_argument("--select", choices=("staged", "streaming"), default="streaming",
                     help="prefill workloads: staged entry points with the score matrix, or dsa_prefill_streaming")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
@@ -804,10 +809,11 @@ def main():
 
 
 def other_workloads(args, att=None):
-    """The mixed-length paged decode and the 32K prefill (streaming selection,
-    then the staged entry points), timed in the same run as the headline
-    (their own roofline fractions beside it; `att`: the headline's
-    attainable-peak measurements, if taken)."""
+    """The mixed-length paged decode, the 32K prefill (streaming selection,
+    then the staged entry points), the 128K chunked prefill and the indexer
+    warm-up objective, timed in the same run as the headline (their own
+    roofline fractions beside it; `att`: the headline's attainable-peak
+    measurements, if taken)."""
     out = {}
     print("[bench] paged_decode_b128_mixed4k_128k", file=sys.stderr, flush=True)
     r, _ = run_bench(args, workload="paged_decode_b128_mixed4k_128k", separate_calls=False, attainable=False)
@@ -841,6 +847,22 @@ def other_workloads(args, att=None):
     q = run_prefill(sargs, attainable=False)
     out["prefill_L32k_staged"] = {k: q[k] for k in ("metric", "value", "unit", "ms_per_step", "steps", "stages_ms",
                                                     "memory")}
+    del q
+    # 128K in 4K-token chunks against the growing cache (streaming selection);
+    # each chunk's stages are timed over two passes after one untimed pass
+    print("[bench] chunked_prefill_L128k_c4k (streaming selection)", file=sys.stderr, flush=True)
+    cargs = argparse.Namespace(**vars(pargs))
+    cargs.workload, cargs.select, cargs.steps = "chunked_prefill_L128k_c4k", "streaming", 2
+    c = run_prefill(cargs, attainable=False)
+    out["chunked_prefill_L128k_c4k"] = {k: c[k] for k in ("metric", "value", "unit", "ms_per_step", "steps",
+                                                          "stages_ms", "indexer", "attention", "memory")}
+    del c
+    print("[bench] warmup_L4k", file=sys.stderr, flush=True)
+    wargs = argparse.Namespace(**vars(args))
+    wargs.workload, wargs.steps, wargs.warmup, wargs.no_cpu_baseline = "warmup_L4k", 5, 2, True
+    w = run_warmup(wargs, att=att or {})
+    out["warmup_L4k"] = {k: w[k] for k in ("metric", "value", "unit", "ms_per_step", "steps", "stages_ms",
+                                           "stages_tflops", "roofline")}
     return out
 
 
