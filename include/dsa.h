@@ -277,9 +277,10 @@ dsa_status dsa_set_attn_splits(int nsplit);
  * indexer pass contracts the FP8 query and key bytes on the FP8 matrix-core
  * form (the pages' FP8 lightning indexer: ouchyi.pink post, DSA paragraph;
  * tenelement.pl "DeepSeek V3.2-Exp Cuts Long-Context Costs", section
- * "Architektura DeepSeek V3.2-Exp: Od MoE do DSA") and scores exactly only
- * the pairs whose FP8 score plus its error bound reaches the row threshold;
- * 0 (the default, the faster one on gfx950): every pair is scored exactly.
+ * "Architektura DeepSeek V3.2-Exp: Od MoE do DSA"); each candidate keeps its
+ * FP8 estimate and error bound, and only the candidates whose bounds straddle
+ * the row's k-th score are scored exactly afterwards; 0 (the default, the
+ * faster one on gfx950): every pair is scored exactly in the filtered pass.
  * The selection is the same either way.
  * Errors: DSA_ERR_SHAPE if `on` is not 0 or 1.
  */

@@ -659,11 +659,12 @@ dsa_status run_stream(const dsa_batch* batch, const uint8_t* q8, const float* q_
   sa.ld_samp = p.ld_samp;
   sa.thr = reinterpret_cast<unsigned long long*>(ws + p.off_thr);
   sa.rowinfo = reinterpret_cast<unsigned long long*>(ws + p.off_info);
-  sa.lists = reinterpret_cast<const uint2*>(ws + p.off_lists);
+  sa.lists = reinterpret_cast<uint2*>(ws + p.off_lists);
   sa.segs = reinterpret_cast<const uint2*>(ws + p.off_segs);
   sa.redo = reinterpret_cast<int*>(ws + p.off_redo);
   sa.redo_count = reinterpret_cast<uint32_t*>(ws + p.off_cnt);
   sa.idx = idx;
+  sa.fp8 = g_indexer_fp8;
   LAUNCH(mark(0), "stage event");
   if (!p.dense) {
     LAUNCH(launch_stream_gather(sa, s), "sampled-key gather launch");

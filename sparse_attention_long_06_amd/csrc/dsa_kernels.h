@@ -85,11 +85,12 @@ struct StreamArgs {
   int64_t ld_samp;
   unsigned long long* thr;
   unsigned long long* rowinfo;
-  const uint2* lists;
+  uint2* lists;          // [T, cap]: the filtered pass's pairs (rewritten in place by the exactify launch)
   const uint2* segs;
   int* redo;             // [T] rows the finalize leaves to the fallback
   uint32_t* redo_count;
   int32_t* idx;          // [T, k]
+  bool fp8 = false;      // the filtered pass ran on FP8 estimates (pairs carry their error bound)
 };
 
 hipError_t launch_stream_gather(const StreamArgs& a, hipStream_t stream);

@@ -416,35 +416,21 @@ __global__ void __launch_bounds__(256) indexer_decode_ring_kernel(IndexerArgs a)
 // flush falls inside the loop.  kshift > 0 runs the kernel over a compacted
 // sample of every 2^kshift-th token (causal bound p >> kshift).
 //
-// F8 (filtered pass only): the scores that decide which pairs are kept come
-// from v_mfma_scale_f32_16x16x128_f8f6f4 on the raw e4m3 bytes (one
-// instruction per 16 heads x 16 keys, 3.3x the measured issue rate of the
-// bf16 form), and only the keys whose FP8 score plus its error bound reaches
-// the row threshold are scored again exactly, with the bf16 arithmetic of the
-// other variants, from the same ring slot.  The FP8 score differs from the
-// exact one by at most kF8ErrRel * 448 * ks * sum_h |w_h qs| max_d |q8_hd|:
-// the matrix core's FP8 dot product is within kF8ErrRel/2 of
-// max_d |q_d| * max_d |k_d| of the exact one (tests pin it at 2^-10), |k8_d|
-// <= 448, ReLU is 1-Lipschitz, and the other half of the budget covers the
-// bf16 path's own fp32 rounding.  So the pairs kept, their keys and the
-// buffer flushes are exactly those of the bf16 filtered pass.
+// F8 (filtered pass only): the scores come from
+// v_mfma_scale_f32_16x16x128_f8f6f4 on the raw e4m3 bytes (one instruction
+// per 16 heads x 16 keys, 3.3x the measured issue rate of the bf16 form) and
+// nothing is rescored here.  The FP8 score differs from the exact one (the
+// bf16 arithmetic of the other variants) by at most m = kF8ErrRel * 448 * ks
+// * sum_h |w_h qs| max_d |q8_hd|: the matrix core's FP8 dot product is within
+// kF8ErrRel/2 of max_d |q_d| * max_d |k_d| of the exact one (tests pin it at
+// 2^-10), |k8_d| <= 448, ReLU is 1-Lipschitz, and the other half of the
+// budget covers the bf16 path's own fp32 rounding.  Every key whose estimate
+// plus m reaches the threshold's key is kept with its estimate and m (so
+// every pair the exact filter keeps is among them), and
+// stream_exactify_kernel settles each row from the bounds estimate +- m.
 constexpr int kPreRing = 6;
 constexpr int kPreKeys = 64;
 constexpr float kF8ErrRel = 0x1p-7f;
-
-// Position of the n-th (from 0) set bit of m; n < popcount(m).
-__device__ __forceinline__ int nth_set_bit(unsigned long long m, int n) {
-  int p = 0;
-#pragma unroll
-  for (int w = 32; w >= 1; w >>= 1) {
-    const int c = __popcll((m >> p) & ((1ull << w) - 1ull));
-    if (n >= c) {
-      n -= c;
-      p += w;
-    }
-  }
-  return p;
-}
 
 // v[g] of four values (selects: an indexed array would go to scratch memory).
 __device__ __forceinline__ float sel4(int g, float v0, float v1, float v2, float v3) {
@@ -734,50 +720,24 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
       }
     }
     if constexpr (F8) {
-      // lane l takes key l of the slot; the keys whose FP8 estimate plus its
-      // bound reaches the row threshold are scored exactly in batches of 16
-      // (column n of a batch: the (16b + n)-th such key, so token order is
-      // kept) and appended when their exact (key, token) order reaches it
+      // lane l takes key l of the slot; a key whose FP8 estimate plus its
+      // bound reaches the row threshold's key is appended with the estimate's
+      // key, its token and its bound rounded up to 14 bits (float bits >> 17)
+      // above the token (tokens < 2^18); stream_exactify_kernel turns the
+      // row's list into exact keys where they decide the selection
       const int sl = kbeg + m * kPreKeys + lane;
       const float ksl = SCALE ? *reinterpret_cast<const float*>(slot + kPreKeys * DI + 4 * lane) : 1.0f;
 #pragma unroll
       for (int r = 0; r < R; ++r) {
         const float xt = sel4(grp, fv[0][r], fv[1][r], fv[2][r], fv[3][r]);
-        const bool maybe = sl <= rpos[r] && score_key(xt + marg[r] * fabsf(ksl)) >= (uint32_t)(rthr[r] >> 32);
+        const float mg = marg[r] * fabsf(ksl);
+        const bool maybe = sl <= rpos[r] && score_key(xt + mg) >= (uint32_t)(rthr[r] >> 32);
+        const uint32_t menc = (__float_as_uint(mg) + ((1u << 17) - 1u)) >> 17;
         const unsigned long long mm = __ballot(maybe);
-        const int cnt = __popcll(mm);
-        for (int b0 = 0; b0 < cnt; b0 += 16) {
-          const int n = b0 + nl;
-          const int q = nth_set_bit(mm, n < cnt ? n : cnt - 1);
-          const int kq = q & 15;
-          const char* krow = slot + (q >> 4) * 16 * DI + kq * DI;
-          Frag<DI> kf;
-          kf.lo = *reinterpret_cast<const v4i*>(krow + 16 * ((2 * grp) ^ kswz(kq)));
-          kf.hi = *reinterpret_cast<const v4i*>(krow + 16 * ((2 * grp + 1) ^ kswz(kq)));
-          const float ks = SCALE ? *reinterpret_cast<const float*>(slot + kPreKeys * DI + 4 * q) : 1.0f;
-          const Wide<DI> kb = widen<DI>(kf);
-          float part = 0.0f;
-#pragma unroll
-          for (int ht = 0; ht < HT; ++ht) {
-            // widened here, per batch: kept widened (loop-invariant, so the
-            // compiler would hoist it) it would cost 128 more registers
-            Frag<DI> qr = q8[r][ht];
-            asm volatile("" : "+v"(qr.lo), "+v"(qr.hi));
-            const v4f acc = mfma_dot<DI>(widen<DI>(qr), kb);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) part = fmaf(wq[r][ht][i], relu(acc[i]), part);
-          }
-          const float x = group_sum(part) * ks;
-          const int sq = kbeg + m * kPreKeys + q;
-          const uint32_t key = score_key(x);
-          const unsigned long long comp = ((unsigned long long)key << 32) | (uint32_t)~(uint32_t)sq;
-          const bool keep = grp == 0 && n < cnt && comp >= rthr[r];
-          const unsigned long long k64 = __ballot(keep);
-          const uint32_t before = __builtin_amdgcn_mbcnt_hi((uint32_t)(k64 >> 32),
-                                                            __builtin_amdgcn_mbcnt_lo((uint32_t)k64, 0u));
-          if (keep) mycand[r * kStreamLds + ccnt[r] + before] = make_uint2(key, (uint32_t)sq);
-          ccnt[r] += (uint32_t)__popcll(k64);
-        }
+        const uint32_t before = __builtin_amdgcn_mbcnt_hi((uint32_t)(mm >> 32),
+                                                          __builtin_amdgcn_mbcnt_lo((uint32_t)mm, 0u));
+        if (maybe) mycand[r * kStreamLds + ccnt[r] + before] = make_uint2(score_key(xt), (uint32_t)sl | (menc << 18));
+        ccnt[r] += (uint32_t)__popcll(mm);
       }
     } else if constexpr (FILT) {
       // lane (g, l) takes key 16g + l of the slot, so the 64 lanes hold the

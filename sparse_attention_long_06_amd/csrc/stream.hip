@@ -202,7 +202,163 @@ struct RowScorer {
       if (grp == 0 && s < n) sc[gi * 16 + nl] = part * ks;
     }
   }
+
+  // Keys of the exact scores of tokens toks[0, nt) (LDS) into keys[] (LDS),
+  // with the arithmetic of stage(); wave w takes groups of 16 tokens w, w +
+  // nwaves, ...
+  __device__ void score_list(const StreamArgs& a, int b, const int* toks, int nt, uint32_t* keys, int wave,
+                             int nwaves, int nl, int grp) const {
+    const int ngroups = (nt + 15) / 16;
+    for (int gi = wave; gi < ngroups; gi += nwaves) {
+      const int i = gi * 16 + nl;
+      const int s = toks[min(i, nt - 1)];
+      Frag<128> kf;
+      load_frag<128, false>(kf, token_ptr(a.g, a.kidx, b, s), grp);
+      const float ks = a.ksc.data ? *reinterpret_cast<const float*>(token_ptr(a.g, a.ksc, b, s)) : 1.0f;
+      const Wide<128> kb = widen<128>(kf);
+      float part = 0.0f;
+#pragma unroll
+      for (int ht = 0; ht < HT; ++ht) {
+        const v4f acc = mfma_dot<128>(qa[ht], kb);
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) part = fmaf(wq[ht][i4], relu(acc[i4]), part);
+      }
+      part = group_sum(part);
+      if (grp == 0 && i < nt) keys[i] = score_key(part * ks);
+    }
+  }
 };
+
+// ---- exact keys for the FP8 filter's candidates
+//
+// With the FP8 filter each pair carries its estimate's key and a bound m on
+// |estimate - exact| (float bits >> 17, rounded up, above the 18-bit token),
+// so the exact score lies in [L, U] = [estimate - m, estimate + m], both
+// rounded outward.  With l_k and u_k the k-th largest L and U over the row's
+// candidates:
+//   L > u_k  the key is in the row's top k whatever the exact scores (fewer
+//            than k other candidates can reach it, and every non-candidate
+//            is below the threshold);
+//   U < l_k  it is not (k candidates are strictly above it);
+//   else     (the band) its exact score is computed from the index-key cache.
+// The pairs are rewritten in place: key 0xFFFFFFFF for the first kind, 0 for
+// the second (neither is the key of a finite score), the exact key for the
+// band, the bare token; the finalize then selects exactly what it would have
+// from exact keys.  Every pair the exact filter keeps is a candidate (its U
+// reaches the threshold's key), so when l_k is above the threshold's key the
+// row's top k are all candidates; otherwise, or when the band exceeds
+// kExBand, the row's count is cleared and the finalize sends it to the
+// fallback.
+constexpr int kExNT = 512;
+constexpr int kExPer = 7168 / kExNT;     // register-held candidates per thread
+constexpr int kExBand = 2048;            // band keys rescored per row at most
+static_assert(kExPer * kExNT >= 7168 && kExPer <= 32, "every candidate held in registers");
+
+// The float next below (above) x, or -2^-126 (2^-126) for |x| < 2^-126: a
+// rounded-to-nearest result stepped once this way bounds the exact value
+// from below (above), also where a result was flushed to zero.
+__device__ __forceinline__ float step_down(float x) {
+  if (!(fabsf(x) >= 0x1p-126f)) return -0x1p-126f;
+  const uint32_t u = __float_as_uint(x);
+  return __uint_as_float(x > 0.0f ? u - 1u : u + 1u);
+}
+__device__ __forceinline__ float step_up(float x) {
+  if (!(fabsf(x) >= 0x1p-126f)) return 0x1p-126f;
+  const uint32_t u = __float_as_uint(x);
+  return __uint_as_float(x > 0.0f ? u + 1u : u - 1u);
+}
+
+template <int HT>
+__global__ void __launch_bounds__(kExNT) stream_exactify_kernel(StreamArgs a) {
+  __shared__ __attribute__((aligned(16))) uint32_t hist[2][kBins1];
+  __shared__ uint32_t tmp[kExNT / 64];
+  __shared__ uint32_t red[kExNT / 64];
+  __shared__ BinSel res;
+  __shared__ int btok[kExBand];
+  __shared__ uint32_t bkey[kExBand];
+
+  const int t = blockIdx.x;
+  int b, pos;
+  row_seq_pos(a.g, t, b, pos);
+  const int n = pos + 1;
+  const uint32_t k = (uint32_t)a.k;
+  if (n <= a.k) return;
+  const unsigned long long info = a.rowinfo[t];
+  const uint32_t total = (uint32_t)info, nseg = (uint32_t)(info >> 32);
+  if (!(total >= k && total <= (uint32_t)a.cap && nseg <= (uint32_t)kStreamMaxSegs)) return;  // the fallback's
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int nl = lane & 15, grp = lane >> 4;
+  RowScorer<HT> rs;
+  rs.init(a, t, nl, grp);
+  uint2* lists = a.lists + (int64_t)t * a.cap;
+  const int i0 = threadIdx.x * kExPer;
+  const int nv = max(0, min(kExPer, (int)total - i0));
+  uint2 e[kExPer];
+#pragma unroll
+  for (int j = 0; j < kExPer; ++j) e[j] = lists[min(i0 + j, (int)total - 1)];   // all in flight
+  uint32_t lk[kExPer], uk[kExPer];
+#pragma unroll
+  for (int j = 0; j < kExPer; ++j) {
+    const float est = key_score(e[j].x);
+    const float mg = __uint_as_float((e[j].y >> 18) << 17);
+    lk[j] = score_key(step_down(est - mg));
+    uk[j] = score_key(step_up(est + mg));
+  }
+  const uint32_t vm = nv >= 32 ? 0xFFFFFFFFu : (1u << nv) - 1u;
+  // the k-th largest of the row's keys `key`: the radix passes end with the
+  // k largest being those above prefix P and all those at it, or with P a
+  // whole key; either way the k-th is the smallest key at prefix P
+  auto kth = [&](const uint32_t (&key)[kExPer]) -> uint32_t {
+    for (int i = threadIdx.x; i < 2 * kBins1; i += kExNT) (&hist[0][0])[i] = 0u;
+    lds_barrier();
+    uint32_t P = 0u, need = k, cnt = total;
+    int pbits = 0;
+    reg_radix<kExNT, kExPer>(key, vm, hist[0], hist[1], &res, P, pbits, need, cnt);
+    uint32_t mn = 0xFFFFFFFFu;
+#pragma unroll
+    for (int j = 0; j < kExPer; ++j)
+      if (((vm >> j) & 1u) && key_prefix(key[j], pbits) == P) mn = min(mn, key[j]);
+    mn = wave_min_u32(mn);
+    if (lane == 0) red[wid] = mn;
+    lds_barrier();
+    uint32_t r = 0xFFFFFFFFu;
+#pragma unroll
+    for (int w = 0; w < kExNT / 64; ++w) r = min(r, red[w]);
+    lds_barrier();                                   // red is free again
+    return r;
+  };
+  const uint32_t lkth = kth(lk);
+  const uint32_t ukth = kth(uk);
+  uint32_t in = 0u, band = 0u;
+#pragma unroll
+  for (int j = 0; j < kExPer; ++j) {
+    const bool v = (vm >> j) & 1u;
+    in |= (v && lk[j] > ukth ? 1u : 0u) << j;
+    band |= (v && !(lk[j] > ukth) && !(uk[j] < lkth) ? 1u : 0u) << j;
+  }
+  uint32_t nb;
+  uint32_t bo = block_exclusive_scan<kExNT>((uint32_t)__popc(band), tmp, nb);
+  const uint32_t thr_key = (uint32_t)(a.thr[t] >> 32);
+  if (!(lkth > thr_key && nb <= (uint32_t)kExBand)) {       // uniform
+    if (threadIdx.x == 0) a.rowinfo[t] = 0ull;              // the finalize lists the row for the fallback
+    return;
+  }
+  const uint32_t bo0 = bo;
+#pragma unroll
+  for (int j = 0; j < kExPer; ++j)
+    if ((band >> j) & 1u) btok[bo++] = (int)(e[j].y & 0x3FFFFu);
+  lds_barrier();                                     // band tokens in
+  rs.score_list(a, b, btok, (int)nb, bkey, wid, kExNT / 64, nl, grp);
+  lds_barrier();                                     // band keys in
+  bo = bo0;
+#pragma unroll
+  for (int j = 0; j < kExPer; ++j) {
+    if (j < nv) {
+      const uint32_t key = ((in >> j) & 1u) ? 0xFFFFFFFFu : ((band >> j) & 1u) ? bkey[bo++] : 0u;
+      lists[i0 + j] = make_uint2(key, e[j].y & 0x3FFFFu);
+    }
+  }
+}
 
 __global__ void __launch_bounds__(kFinNT) stream_finalize_kernel(StreamArgs a) {
   __shared__ uint32_t hist[kBins1];
@@ -444,6 +600,17 @@ hipError_t launch_stream_threshold(const StreamArgs& a, hipStream_t stream) {
 }
 
 hipError_t launch_stream_finalize(const StreamArgs& a, hipStream_t stream) {
+  if (a.fp8) {
+    switch ((a.H_I + 15) / 16) {
+      case 1: hipLaunchKernelGGL(stream_exactify_kernel<1>, dim3(a.g.num_rows), dim3(kExNT), 0, stream, a); break;
+      case 2: hipLaunchKernelGGL(stream_exactify_kernel<2>, dim3(a.g.num_rows), dim3(kExNT), 0, stream, a); break;
+      case 3: hipLaunchKernelGGL(stream_exactify_kernel<3>, dim3(a.g.num_rows), dim3(kExNT), 0, stream, a); break;
+      case 4: hipLaunchKernelGGL(stream_exactify_kernel<4>, dim3(a.g.num_rows), dim3(kExNT), 0, stream, a); break;
+      default: return hipErrorInvalidValue;
+    }
+    const hipError_t e0 = hipGetLastError();
+    if (e0 != hipSuccess) return e0;
+  }
   hipLaunchKernelGGL(stream_finalize_kernel, dim3(a.g.num_rows), dim3(kFinNT), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

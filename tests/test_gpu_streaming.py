@@ -110,11 +110,12 @@ FP8_CASES = [CASES[1], CASES[4], CASES[6], CASES[8]]
 
 @pytest.mark.parametrize("wl", FP8_CASES, ids=[w.name for w in FP8_CASES])
 def test_fp8_filter_equals_exact_filter(wl):
-    """With dsa_set_indexer_fp8(1) the filtered pass decides on FP8
-    matrix-core scores plus their error bound and keeps on exact ones (the
-    16x16x32 kernels' arithmetic, which every prefill pass of the call then
-    uses).  Its kept pairs, hence the selection and the attention over it,
-    must equal the stored-score path's bit for bit, and the oracle's."""
+    """With dsa_set_indexer_fp8(1) the filtered pass keeps every pair whose
+    FP8 matrix-core estimate plus its error bound reaches the threshold, and
+    only the pairs whose bounds straddle the row's k-th score are scored
+    exactly afterwards (the 16x16x32 kernels' arithmetic).  The selection, and
+    the attention over it, must equal the stored-score path's bit for bit, and
+    the oracle's."""
     announce("fp8 filter vs stored scores", wl.name)
     inp = W.generate(wl, DEV)
     try:
