@@ -19,6 +19,8 @@
 //              rows with n <= cap take thr = 0 (every token), rows with
 //              n <= k need none;
 //   [filtered indexer: pairs with c >= thr go to segment lists]
+//   exactify   (FP8 filter only) per row, the pairs' FP8 estimates become
+//              exact keys where they decide the selection (see below);
 //   finalize   per row, the segments sorted by (chunk, flush) give the
 //              candidates in token order; the same radix select and ordered
 //              compaction as the top-k kernels picks the k largest.
