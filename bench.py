@@ -401,6 +401,7 @@ def run_prefill(args, attainable=True):
     import sparse_attention_long_06_amd as dsa
 
     wl = W.BY_NAME[args.workload]
+    dsa.set_indexer_fp8(bool(getattr(args, "indexer_fp8", False)) and args.select == "streaming")
     if wl.chunk:
         return run_chunked(args, wl)
     dev = torch.device("cuda:0")
@@ -469,7 +470,9 @@ def run_prefill(args, attainable=True):
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp8-storage/bf16-mfma",
         "data": "synthetic (seeded N(0,1) draws, per-token e4m3fn quantised indexer q/k; bf16 latent KV)",
         "config": {"workload": wl.name, "rows": T, "context": wl.seq_len, "k": wl.k, "H_I": wl.H_I, "d_I": wl.d_I,
-                   "H": wl.H, "D": wl.D, "D_v": wl.D_v, "selection": args.select, "parallelism": "single GPU"},
+                   "H": wl.H, "D": wl.D, "D_v": wl.D_v, "selection": args.select,
+                   "indexer_fp8": bool(getattr(args, "indexer_fp8", False)) and args.select == "streaming",
+                   "parallelism": "single GPU"},
         "stages_ms": {k: round(v, 3) for k, v in st.items()},
         "memory": mem,
         "indexer": {"causal_pairs": pairs, "TFLOP/s": round(idx_tf, 1), "fp8_peak_frac": round(idx_tf / 5000.0, 4),
@@ -561,7 +564,9 @@ def run_chunked(args, wl):
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp8-storage/bf16-mfma",
         "data": "synthetic (seeded N(0,1) draws, per-token e4m3fn quantised indexer q/k; bf16 latent KV)",
         "config": {"workload": wl.name, "rows": rows, "context": wl.seq_len, "chunk": wl.chunk, "k": wl.k,
-                   "selection": args.select, "parallelism": "single GPU"},
+                   "selection": args.select,
+                   "indexer_fp8": bool(getattr(args, "indexer_fp8", False)) and args.select == "streaming",
+                   "parallelism": "single GPU"},
         "stages_ms": {k: round(v, 3) for k, v in st.items()},
         "memory": {("workspace_bytes" if args.select == "streaming" else "score_matrix_bytes"): peak_ws},
         "indexer": {"causal_pairs": pairs, "TFLOP/s": round(idx_tf, 1), "fp8_peak_frac": round(idx_tf / FP8_PEAK_TFLOPS, 4),
@@ -779,6 +784,8 @@ def main():
                          "lines of the default run")
     ap.add_argument("--select", choices=("staged", "streaming"), default="streaming",
                     help="prefill workloads: staged entry points with the score matrix, or dsa_prefill_streaming")
+    ap.add_argument("--indexer-fp8", action="store_true",
+                    help="prefill workloads with --select streaming: the FP8 filter (dsa_set_indexer_fp8(1))")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--copy-calibration", type=int, default=0)
     args = ap.parse_args()
