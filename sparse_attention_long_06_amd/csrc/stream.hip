@@ -207,26 +207,40 @@ struct RowScorer {
 
   // Keys of the exact scores of tokens toks[0, nt) (LDS) into keys[] (LDS),
   // with the arithmetic of stage(); wave w takes groups of 16 tokens w, w +
-  // nwaves, ...
+  // nwaves, ..., gathering kGather groups' keys before scoring any of them.
+  static constexpr int kGather = 4;
   __device__ void score_list(const StreamArgs& a, int b, const int* toks, int nt, uint32_t* keys, int wave,
                              int nwaves, int nl, int grp) const {
     const int ngroups = (nt + 15) / 16;
-    for (int gi = wave; gi < ngroups; gi += nwaves) {
-      const int i = gi * 16 + nl;
-      const int s = toks[min(i, nt - 1)];
-      Frag<128> kf;
-      load_frag<128, false>(kf, token_ptr(a.g, a.kidx, b, s), grp);
-      const float ks = a.ksc.data ? *reinterpret_cast<const float*>(token_ptr(a.g, a.ksc, b, s)) : 1.0f;
-      const Wide<128> kb = widen<128>(kf);
-      float part = 0.0f;
+    for (int g0 = wave; g0 < ngroups; g0 += nwaves * kGather) {
+      Frag<128> kf[kGather];
+      float ks[kGather];
 #pragma unroll
-      for (int ht = 0; ht < HT; ++ht) {
-        const v4f acc = mfma_dot<128>(qa[ht], kb);
-#pragma unroll
-        for (int i4 = 0; i4 < 4; ++i4) part = fmaf(wq[ht][i4], relu(acc[i4]), part);
+      for (int u = 0; u < kGather; ++u) {
+        const int gi = g0 + u * nwaves;
+        if (gi < ngroups) {                          // uniform over the wave
+          const int s = toks[min(gi * 16 + nl, nt - 1)];
+          load_frag<128, false>(kf[u], token_ptr(a.g, a.kidx, b, s), grp);
+          ks[u] = a.ksc.data ? *reinterpret_cast<const float*>(token_ptr(a.g, a.ksc, b, s)) : 1.0f;
+        }
       }
-      part = group_sum(part);
-      if (grp == 0 && i < nt) keys[i] = score_key(part * ks);
+#pragma unroll
+      for (int u = 0; u < kGather; ++u) {
+        const int gi = g0 + u * nwaves;
+        if (gi < ngroups) {
+          const int i = gi * 16 + nl;
+          const Wide<128> kb = widen<128>(kf[u]);
+          float part = 0.0f;
+#pragma unroll
+          for (int ht = 0; ht < HT; ++ht) {
+            const v4f acc = mfma_dot<128>(qa[ht], kb);
+#pragma unroll
+            for (int i4 = 0; i4 < 4; ++i4) part = fmaf(wq[ht][i4], relu(acc[i4]), part);
+          }
+          part = group_sum(part);
+          if (grp == 0 && i < nt) keys[i] = score_key(part * ks[u]);
+        }
+      }
     }
   }
 };
