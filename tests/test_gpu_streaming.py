@@ -241,12 +241,21 @@ def _crafted(kind):
     return inp
 
 
+@pytest.mark.parametrize("fp8", [False, True], ids=["exact_filter", "fp8_filter"])
 @pytest.mark.parametrize("kind", ["underfill", "overflow", "zero_rows"])
-def test_streaming_fallbacks_bit_exact(kind):
-    announce("streaming prefill crafted", kind)
+def test_streaming_fallbacks_bit_exact(kind, fp8):
+    """Crafted rows that leave the finalize too few candidates, too many, or
+    none but ties, so that the fallback recomputes them; with the FP8 filter
+    the exactify launch must leave such rows to it (and send there any row
+    whose k-th lower bound does not clear the threshold)."""
+    announce("streaming prefill crafted", kind, "fp8" if fp8 else "exact")
     inp = _crafted(kind)
     wl = inp.wl
-    p, s = _both(inp)
+    try:
+        dsa.set_indexer_fp8(fp8)
+        p, s = _both(inp)
+    finally:
+        dsa.set_indexer_fp8(False)
     _assert_same(p, s, f"crafted {kind}")
     idx, out, lse = (to_np(x) for x in s)
     n_rows = inp.num_rows
